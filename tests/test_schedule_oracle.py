@@ -1,0 +1,78 @@
+"""Pins of the split-KV schedule rule (the oracle side of the scheduler).
+
+The pages fix only the table shapes (FlashMLA interface page, docstring of
+get_mla_metadata); the rule is ours.  It is pinned by the invariants any
+correct schedule must meet (coverage exactly once and in order, per-part cost
+bound, split counts, split-index bookkeeping), and the invariant checker is
+itself pinned by planting mistakes in valid tables.
+"""
+import numpy as np
+import pytest
+
+from oracle import check_schedule, schedule
+from workloads import make_config
+
+
+def _cases():
+    rng = np.random.default_rng(0)
+    yield [127, 300], 4, 2
+    yield [0], 1, 1
+    yield [0, 0, 0], 8, 2
+    yield [1] * 10, 3, 1
+    yield [65536] + [512] * 31, 256, 3
+    for _ in range(60):
+        B = int(rng.integers(1, 40))
+        L = rng.integers(0, 3000, size=B)
+        L[rng.random(B) < 0.2] = 0
+        yield L.tolist(), int(rng.integers(1, 300)), int(rng.integers(1, 6))
+
+
+@pytest.mark.parametrize("L,parts,fc", list(_cases()))
+def test_schedule_invariants(L, parts, fc):
+    md, ns = schedule(L, parts, fc)
+    assert check_schedule(md, ns, L, parts, fc)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_schedule_on_config_lengths(cfg):
+    L = make_config(cfg).cache_seqlens if cfg != 4 else make_config(4).cache_seqlens
+    for parts in (1, 7, 64, 256, 1024):
+        md, ns = schedule(L, parts, 2)
+        check_schedule(md, ns, L, parts, 2)
+        W = int(md[0, 5])
+        total = int(sum(-(-int(x) // 64) for x in L)) + 2 * len(L)
+        assert W == -(-total // parts)
+
+
+def test_single_part_takes_everything_in_one_split_each():
+    L = [5, 700, 0, 64]
+    md, ns = schedule(L, 1, 2)
+    assert ns.tolist() == [0, 1, 2, 3, 4]
+    assert md[0, :5].tolist() == [0, 0, 3, 1, 0]
+
+
+def test_long_sequence_is_spread_over_many_parts():
+    L = make_config(4).cache_seqlens
+    md, ns = schedule(L, 256, 2)
+    assert ns[1] - ns[0] > 100          # the 65536-token sequence is split widely
+
+
+@pytest.mark.parametrize("mutation", ["drop_page", "dup_page", "bad_rank", "bad_count", "overload"])
+def test_checker_catches_planted_mistakes(mutation):
+    L = [300, 129, 64, 1000]
+    md, ns = schedule(L, 6, 2)
+    md = md.copy()
+    ns = ns.copy()
+    if mutation == "drop_page":
+        md[0, 3] -= 1
+    elif mutation == "dup_page":
+        md[1, 1] -= 1
+    elif mutation == "bad_rank":
+        k = next(p for p in range(6) if md[p, 4] > 0)
+        md[k, 4] += 1
+    elif mutation == "bad_count":
+        ns[2:] += 1
+    elif mutation == "overload":
+        md[:, 5] = 1                      # claimed payload too small for the real costs
+    with pytest.raises(AssertionError):
+        check_schedule(md, ns, L, 6, 2)
