@@ -1,0 +1,190 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA decode library
+ * (libmla_decode.so).
+ *
+ * Multi-head latent attention decode over a paged KV cache.  Every query
+ * token has num_heads_q heads of width head_dim = 576: a 512-wide latent part
+ * followed by a 64-wide rope part.  All heads of one KV group attend to one
+ * shared cached row per key; V is the first head_dim_v = 512 columns of those
+ * same rows.
+ *
+ * Sources (web pages; cited by title and section):
+ *   - FlashMLA interface page (flash_mla_interface.py): docstrings of
+ *     get_mla_metadata and flash_mla_with_kvcache -- argument shapes, the
+ *     default scale 1/sqrt(head_dim), the causal flag, the outputs out and
+ *     softmax_lse, and the metadata/attention call pair.
+ *   - vLLM vllm.attention.ops.flashmla page: the same two calls; the
+ *     platform gate is_flashmla_supported returning (supported, reason).
+ *   - FlashInfer trtllm_batch_decode_with_kv_cache_mla page: query is
+ *     q_nope ++ q_rope, the cache is ckv ++ kpe (512 + 64); caller-provided
+ *     out; the note on fused fp8 scales bmm1/bmm2.
+ *   - Ascend ATB MLA page (AtbMLAGetWorkspaceSize / AtbMLA): a status-code C
+ *     API with a workspace-size query before the run.
+ *
+ * Conventions for every entry point:
+ *   - Plain C types; device buffers are device pointers (hipMalloc'd or
+ *     torch-owned); `stream` is a hipStream_t passed as void* (NULL = the
+ *     default stream).
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; device calls only enqueue work on `stream`.
+ *   - All arguments are validated on the host before any HIP call; on error
+ *     nothing is enqueued and a non-zero mla_status is returned.  No entry
+ *     point throws or aborts.
+ *   - Layouts are dense row-major (C order) with the shapes given below.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Ints per row of the tile-scheduler table ("TileSchedulerMetaDataSize"). */
+#define MLA_TILE_MD_INTS 8
+/* Fixed shape of the absorbed-MLA problem (FlashInfer MLA page: kv_lora_rank
+ * 512, qk_rope_head_dim 64). */
+#define MLA_HEAD_DIM 576
+#define MLA_HEAD_DIM_V 512
+#define MLA_PAGE_BLOCK_SIZE 64
+/* Largest batch the scheduler kernel accepts. */
+#define MLA_MAX_BATCH 8192
+/* Largest rows per KV head (s_q * num_heads_q / num_heads_k). */
+#define MLA_MAX_ROWS 1024
+
+enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,         /* null pointer, non-positive size, inconsistent sizes */
+  MLA_ERR_UNSUPPORTED = 2,         /* valid request this build does not implement, or a non-gfx950 device */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < mla_workspace_bytes(...) */
+  MLA_ERR_NO_DEVICE = 4,           /* no HIP device visible */
+  MLA_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+};
+
+enum mla_kv_dtype {
+  MLA_KV_BF16 = 0,        /* cache rows are bf16 */
+  MLA_KV_FP8_E4M3FN = 1   /* cache rows are OCP FP8 E4M3 codes (finite max 448) */
+};
+
+/* Human-readable text for a status code (static storage; never NULL).  The
+ * UNSUPPORTED text of the last failing call on this thread names the reason,
+ * as the vLLM platform gate returns (supported, reason). */
+const char *mla_status_str(int status);
+
+/* Host only.  Recommended balancing target (parts) for this head layout on
+ * the current device: about one workgroup per compute unit, divided among the
+ * row tiles and KV heads.  The tile table then has batch + num_parts - 1 rows.
+ *   heads_per_head_k = s_q * num_heads_q / num_heads_k  (FlashMLA interface
+ *   page, get_mla_metadata: num_heads_per_head_k).
+ * Writes *num_parts; returns MLA_OK, INVALID_ARG, NO_DEVICE or UNSUPPORTED. */
+int mla_num_parts(int batch, int heads_per_head_k, int num_heads_k, int *num_parts);
+
+/* Device, asynchronous on `stream`.  The split-KV tile scheduler
+ * (FlashMLA interface page, get_mla_metadata: returns
+ * tile_scheduler_metadata (num_sm_parts, TileSchedulerMetaDataSize) int32 and
+ * num_splits (batch + 1) int32).
+ *   cache_seqlens : device int32[batch], keys per sequence (>= 0).
+ *   num_parts     : balancing target P >= 1, the number of equal-cost parts
+ *                   the work is cut into (mla_num_parts gives the recommended
+ *                   one); mla_decode_fwd must get the same value.
+ *   tile_md       : device int32[(batch + num_parts - 1) * MLA_TILE_MD_INTS],
+ *                   written; one row per split (the most splits possible is
+ *                   batch + num_parts - 1).
+ *   num_splits    : device int32[batch + 1], written: an exclusive prefix
+ *                   sum, num_splits[0] = 0 and num_splits[b+1]-num_splits[b]
+ *                   >= 1 is the number of splits of sequence b.
+ * Row num_splits[b] + k of tile_md describes split k of sequence b:
+ * [b, first page, end page (exclusive), k, splits of b, payload W,
+ * fixed_cost, part]; rows past the last split hold b = -1.
+ * The table depends only on cache_seqlens, the head layout and num_parts, so
+ * one call serves every layer of a decode step.  No device-to-host
+ * synchronisation happens. */
+int mla_get_metadata(const int32_t *cache_seqlens, int batch, int heads_per_head_k, int num_heads_k,
+                     int32_t *tile_md, int num_parts, int32_t *num_splits, void *stream);
+
+/* As mla_get_metadata with an explicit per-split overhead `fixed_cost`
+ * (in page units, >= 1) of the balancing cost model.  Sequence b costs
+ * fixed_cost + ceil(L_b / 64) units; units are laid end to end in batch
+ * order and cut into num_parts equal ranges of W = ceil(total / num_parts)
+ * units. */
+int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int heads_per_head_k, int num_heads_k,
+                        int num_parts, int fixed_cost, int32_t *tile_md, int32_t *num_splits, void *stream);
+
+/* Host only.  Bytes of split workspace mla_decode_fwd needs (fp32 partial
+ * outputs and log-sum-exps of up to batch + num_parts - 1 splits), written
+ * to *bytes.  Returns MLA_OK or INVALID_ARG. */
+int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, int head_dim_v, int num_parts,
+                        size_t *bytes);
+
+/* Device, asynchronous on `stream`.  MLA decode attention
+ * (FlashMLA interface page, flash_mla_with_kvcache; the pages' native call
+ * takes q, k_cache, head_dim_v, cache_seqlens, block_table, softmax_scale,
+ * causal, tile_scheduler_metadata, num_splits).
+ *   q            : device bf16 [batch][s_q][num_heads_q][head_dim].
+ *   kv_cache     : device [num_blocks][page_block_size][num_heads_k][head_dim],
+ *                  bf16 or e4m3fn codes per kv_dtype.  Token t of sequence b
+ *                  is row t % page_block_size of block
+ *                  block_table[b][t / page_block_size].
+ *   block_table  : device int32 [batch][max_blocks_per_seq].  Entries past
+ *                  ceil(cache_seqlens[b] / page_block_size) are never read;
+ *                  the rest must lie in [0, num_blocks) (not checked: that
+ *                  would need a device read).  Cache rows past
+ *                  cache_seqlens[b] in a sequence's last block are never read.
+ *   cache_seqlens: device int32 [batch], 0 <= L_b <= max_blocks_per_seq * 64.
+ *   softmax_scale: factor on q.k before the softmax (bmm1_scale for an fp8
+ *                  cache).  The Python wrapper supplies 1/sqrt(head_dim) when
+ *                  the caller gives none, as the pages' wrappers do.
+ *   v_scale      : factor on the weighted sum of V (bmm2_scale; 1 for bf16).
+ *   causal       : 0 or 1.  Query i of s_q sees keys t < L_b - s_q + 1 + i
+ *                  (bottom-right alignment).  A row with no visible key gets
+ *                  out = 0 and lse = -inf.
+ *   tile_md, num_parts, num_splits: from mla_get_metadata for these
+ *                  cache_seqlens and this head layout (tile_md has
+ *                  batch + num_parts - 1 rows).
+ *   workspace    : device buffer of >= mla_workspace_bytes(...) bytes,
+ *                  contents ignored on entry.
+ *   out          : device bf16 [batch][s_q][num_heads_q][head_dim_v], written.
+ *   lse          : device fp32 [batch][num_heads_q][s_q], written: natural
+ *                  log of sum_t exp(softmax_scale * q.k_t).
+ * q head h uses KV head h / (num_heads_q / num_heads_k).
+ * Requires head_dim = 576, head_dim_v = 512, page_block_size = 64, a gfx950
+ * device, and s_q * num_heads_q / num_heads_k <= MLA_MAX_ROWS. */
+int mla_decode_fwd(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                   const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                   const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                   int head_dim_v, float softmax_scale, float v_scale, int causal,
+                   const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                   void *workspace, size_t workspace_bytes,
+                   void *out, float *lse, void *stream);
+
+/* The two stages of mla_decode_fwd, for callers that time or overlap them
+ * (same arguments and validation as mla_decode_fwd).
+ *   mla_decode_splits : attention over every split of the tile table; writes
+ *                       out / lse of sequences with one split and the fp32
+ *                       partials (normalised output and log-sum-exp) of the
+ *                       others into the workspace.
+ *   mla_combine_splits: merges the partials of sequences with more than one
+ *                       split by their log-sum-exps into out / lse.  Must run
+ *                       after mla_decode_splits with the same arguments. */
+int mla_decode_splits(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                      const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                      const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                      int head_dim_v, float softmax_scale, float v_scale, int causal,
+                      const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                      void *workspace, size_t workspace_bytes,
+                      void *out, float *lse, void *stream);
+int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                       const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                       const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                       int head_dim_v, float softmax_scale, float v_scale, int causal,
+                       const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                       void *workspace, size_t workspace_bytes,
+                       void *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

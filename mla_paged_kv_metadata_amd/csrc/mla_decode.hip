@@ -1,0 +1,488 @@
+// MLA decode over a paged KV cache on gfx950 (MI355X): split-KV attention
+// kernel and log-sum-exp combine.
+//
+// What is computed (FlashMLA interface page, docstring of
+// flash_mla_with_kvcache): for every sequence b, query token i and head h,
+//   out[b,i,h,:] = sum_t softmax_t(scale * q[b,i,h,:] . k_t) * v_t,
+//   lse[b,h,i]   = ln sum_t exp(scale * q . k_t),
+// where k_t is the 576-wide cached row of token t (fetched through
+// block_table, 64 tokens per page) and v_t is its first 512 columns
+// (FlashInfer MLA page: the cache is ckv ++ kpe and the wrappers pass no
+// separate V cache).
+//
+// Design (per workgroup of 4 waves, 1 workgroup per CU):
+//  * A workgroup owns one split of one sequence (a row of the scheduler
+//    table: a contiguous page range) for a 128-row tile of one KV head; each
+//    wave owns 32 rows (query heads, with s_q folded into rows).
+//  * Pages are streamed HBM -> LDS with 16-byte LDS-DMA loads
+//    (global_load_lds_dwordx4), double buffered (2 x 72 KiB).  Chunks are
+//    XOR-swizzled within each 1152-byte row so that MFMA operand reads hit
+//    distinct banks.
+//  * Scores are computed transposed, S^T[token][head] = K Q^T, on
+//    v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T resident in VGPRs.
+//    In that layout each lane holds one head and 32 of the page's 64 tokens,
+//    so the online-softmax row max/sum is a per-lane loop plus one exchange
+//    with lane ^ 32.
+//  * O^T[dim][head] = V^T P^T on the same MFMA, V^T read from the very same
+//    LDS rows (columns 0..511) with ds_read_b64_tr_b16 transposing loads, P^T
+//    straight from the score registers (the token order inside one k-step is
+//    permuted identically on both operands).  Each lane's 256 accumulators
+//    belong to one head, so the softmax rescale is a per-lane scalar.
+//  * Softmax runs in base 2 with log2(e) folded into the scale.
+//  * A sequence with one split writes bf16 out / fp32 lse directly; a split
+//    sequence writes fp32 partials (O/l, lse) that the combine kernel merges.
+//  * fp8 (e4m3fn) caches are DMA'd as codes into a staging buffer and
+//    widened exactly to bf16 in LDS (every e4m3fn value is a bf16 value);
+//    the fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
+//    softmax_scale and v_scale.
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kRowChunks = kHeadDim * 2 / 16;        // 72 chunks of 16 B per bf16 row
+constexpr int kPageBytes = kPage * kHeadDim * 2;     // 73728
+constexpr int kPageLoads = kPage * kRowChunks / kThreads;   // 18 DMA loads per thread per bf16 page
+constexpr int kF8RowChunks = kHeadDim / 16;          // 36 chunks per fp8 row
+constexpr int kF8PageBytes = kPage * kHeadDim;       // 36864
+constexpr int kF8PageLoads = kPage * kF8RowChunks / kThreads;  // 9
+constexpr int kKSteps = kHeadDim / 16;               // 36 k-steps of the QK^T MFMA
+constexpr int kOTiles = kHeadDimV / 32;              // 16 output tiles of 32 dims
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+static_assert(kPage * kRowChunks % kThreads == 0, "page must split evenly over threads");
+static_assert(kPage * kF8RowChunks % kThreads == 0, "fp8 page must split evenly over threads");
+
+// LDS layout of a bf16 page: nine column groups of 8 chunks (16 B each);
+// group j holds chunks 8j..8j+7 of all 64 tokens, 128 B per token, with the
+// chunk index XOR-swizzled by token & 7.  Returns the 16-byte chunk index of
+// (token t, logical chunk c).  One wave-wide 1 KiB LDS-DMA store then covers
+// 8 whole tokens of one group, so every lane's global source offset is a
+// lane constant plus a wave-uniform term.
+__device__ __forceinline__ int pos_bf16(int t, int c) { return (c >> 3) * 512 + t * 8 + ((c & 7) ^ (t & 7)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above.
+// Wave instruction I covers group I/8, tokens 8*(I%8) .. +7.  Rows >= nvalid
+// (past the sequence end) are replaced by row nvalid-1 so that undefined
+// cache bytes never reach LDS.
+__device__ __forceinline__ void dma_page_bf16(const uint8_t *tok0, int tok_stride, int nvalid,
+                                              LDS_AS uint8_t *dst, int wave, int lane) {
+  const int lt = lane >> 3;
+  const int lane_chunk = ((lane & 7) ^ lt) * 16;
+  if (nvalid == kPage) {
+    const int lane_off = lt * tok_stride + lane_chunk;
+#pragma unroll
+    for (int k = 0; k < kPageLoads; ++k) {
+      const int I = wave * kPageLoads + k;
+      const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
+      __builtin_amdgcn_global_load_lds((const void *)(src + lane_off), (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPageLoads; ++k) {
+      const int I = wave * kPageLoads + k;
+      const int t = min((I & 7) * 8 + lt, nvalid - 1);
+      const uint8_t *src = tok0 + (I >> 3) * 128;
+      __builtin_amdgcn_global_load_lds((const void *)(src + t * tok_stride + lane_chunk),
+                                       (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: wave
+// instruction I covers chunks 4*(I/4) .. +3 of tokens 16*(I%4) .. +15.
+__device__ __forceinline__ void dma_page_fp8(const uint8_t *tok0, int tok_stride, int nvalid,
+                                             LDS_AS uint8_t *dst, int wave, int lane) {
+  const int lt = lane >> 2;
+  const int lane_chunk = (lane & 3) * 16;
+#pragma unroll
+  for (int k = 0; k < kF8PageLoads; ++k) {
+    const int I = wave * kF8PageLoads + k;
+    const int t = min((I & 3) * 16 + lt, nvalid - 1);
+    const uint8_t *src = tok0 + (I >> 2) * 64;
+    __builtin_amdgcn_global_load_lds((const void *)(src + t * tok_stride + lane_chunk),
+                                     (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
+  }
+}
+
+// Two floats that hold bf16-exact values -> packed bf16 pair (truncation is exact here).
+__device__ __forceinline__ unsigned pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Widen the staged fp8 page into the bf16 page layout.  Thread (wave, lane)
+// owns staging chunks of instruction I = 4k + wave: token 16*wave + lane/4,
+// fp8 chunk 4k + lane%4 -> bf16 chunks 2c and 2c + 1 of that token.
+__device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_AS uint8_t *page, int wave,
+                                               int lane) {
+  const int t = 16 * wave + (lane >> 2);
+#pragma unroll
+  for (int k = 0; k < kF8PageLoads; ++k) {
+    const int c = 4 * k + (lane & 3);
+    const u32x4 v = *(const LDS_AS u32x4 *)(stage + ((4 * k + wave) * 64 + lane) * 16);
+    unsigned w[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
+      w[2 * i] = pack_bf16_exact(lo[0], lo[1]);
+      w[2 * i + 1] = pack_bf16_exact(hi[0], hi[1]);
+    }
+    *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c) * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c + 1) * 16) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+
+// One 64-token page for this wave's 32 rows, processed as two 32-token
+// halves: scores, online softmax, PV.
+//   key0 : sequence index of the page's first token; nvis: keys this lane's row may see.
+// Reference max: a row's reference m is fixed by its first visible keys and
+// probabilities are exp2(x - m).  They may exceed 1; that is exact (O and l
+// share the reference) and safe while x - m <= kRefSlackLog2 (p <= 2^64, far
+// from fp32/bf16 overflow).  A score beyond that slack does not rescale O in
+// place (that would drag the 256 accumulators through the VGPR file); the row
+// records the larger reference in m_restart and the caller re-runs the
+// sequence segment from its first page.  Each re-run raises a reference by
+// more than 64, so re-runs are finite, and they never happen unless a later
+// score exceeds the first keys' maximum by 64/log2(e) ~ 44 natural-log units.
+constexpr float kRefSlackLog2 = 64.0f;
+
+// c + 0 * 0 on the matrix core: produces zeroed accumulators in the MFMA
+// accumulation registers.
+__device__ __forceinline__ f32x16 mfma_zero() {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{}, bf16x8{}, f32x16{}, 0, 0, 0);
+}
+
+// S^T accumulation steps on the matrix core with the accumulator pinned to
+// ordinary VGPRs: the O^T accumulators fill all 256 AGPRs, and the compiler
+// would otherwise place S^T there too and spill an O^T tile.  The first step
+// takes an inline zero accumulator; the destination is early-clobber (a
+// 32x32 MFMA destination may not overlap its A/B sources).  mfma_qk_drain
+// supplies the wait states between the last matrix-core write of S^T and
+// its first VALU read (19 > the 8-pass XDL requirement).
+__device__ __forceinline__ void mfma_qk_first(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk_drain(f32x16 &s) {
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s));
+}
+
+// Returns true (wave-uniform) when some row of this wave needs a re-run.
+__device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
+                                            f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
+                                            int lane, int key0, int nvis, float scale_log2) {
+  const int hl = lane >> 5;
+  const int r = lane & 31;
+  bool need_any = false;
+
+  // K operand: logical chunk 2*ks + hl of token r (+32 per half) sits at byte
+  // 8192*(ks/4) + 128*r + 16*((2*(ks%4) + hl) ^ (r & 7)) (+4096 per half):
+  // four lane bases, the rest immediates.
+  const LDS_AS uint8_t *kb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) kb[v] = pg + r * 128 + ((2 * v + hl) ^ (r & 7)) * 16;
+
+  // V^T operand via transposing reads: in each 16-lane group, lane i gets
+  // element i%4 of the 8-byte rows loaded by lanes 4r + i/4 (r = 0..3).
+  // Lane (group g, slot 4*rr + qd) loads token 16*ks + 4*(g/2) + rr (+8 for
+  // k-slots 4..7) at dims 32*mt + 16*(g%2) + 4*qd.  With x = 4*(g/2) + rr =
+  // token & 7 and y = 2*(g%2) + qd/2, the byte offset is
+  //   8192*(mt/2) + 2048*ks + 128*x + 64*((mt%2) ^ (g/2)) + 16*(y ^ rr) + 8*(qd%2)
+  // (+1024 for k-slots 4..7), so two lane bases (even / odd mt) plus
+  // immediates address all reads.
+  const int g = lane >> 4, s16 = lane & 15, rr = s16 >> 2, qd = s16 & 3;
+  const int xb = g >> 1;
+  const int lane_ofs = (4 * xb + rr) * 128 + ((2 * (g & 1) + (qd >> 1)) ^ rr) * 16 + (qd & 1) * 8;
+  const LDS_AS uint8_t *vb_even = pg + lane_ofs + 64 * xb;
+  const LDS_AS uint8_t *vb_odd = pg + lane_ofs + 64 * (1 - xb);
+
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    // S^T half: lane holds head r, tokens 32*th + (i/4)*8 + 4*hl + i%4.
+    f32x16 s;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8 ak = *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + th * 4096);
+      if (ks == 0) mfma_qk_first(s, ak, qf[ks]);
+      else mfma_qk(s, ak, qf[ks]);
+    }
+    mfma_qk_drain(s);
+    float x[16];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = s[i] * scale_log2;
+      if (key0 + 32 * th + (i >> 2) * 8 + hl * 4 + (i & 3) >= nvis) x[i] = kNegInf;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (m == kNegInf) m = mx;                       // first visible keys fix the reference
+    const bool need = mx > m + kRefSlackLog2;
+    if (need) m_restart = fmaxf(m_restart, mx);
+    need_any |= need;
+    const float mu = (m == kNegInf) ? 0.f : m;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = __builtin_amdgcn_exp2f(x[i] - mu);
+      ps += x[i];
+    }
+    ps += __shfl_xor(ps, 32);
+    l += ps;
+
+    // P^T operand for k-step 2*th + k: score registers 8*k .. 8*k+7.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[k][e] = (__bf16)x[8 * k + e];
+
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ks = 2 * th + k;
+#pragma unroll
+      for (int mt = 0; mt < kOTiles; ++mt) {
+        const LDS_AS uint8_t *vb = (mt & 1) ? vb_odd : vb_even;
+        const int ofs = 8192 * (mt >> 1) + 2048 * ks;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + ofs));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + ofs + 1024));
+        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[k], o[mt], 0, 0, 0);
+      }
+    }
+  }
+  return __ballot(need_any) != 0;
+}
+
+// Number of passes a segment may take when a score overshoots the reference
+// max by more than kRefSlackLog2 (see attend_page).  Bounded so that a
+// workgroup always terminates; a further overshoot in the last pass is
+// accumulated as is (still finite up to 2^64 relative weights).
+constexpr int kMaxPasses = 4;
+
+template <bool kFp8>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+  LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
+  // bf16: two page buffers.  fp8: one bf16 page + two fp8 staging buffers.
+  LDS_AS uint8_t *page0 = smem;
+  LDS_AS uint8_t *page1 = smem + kPageBytes;
+  LDS_AS uint8_t *stage0 = smem + kPageBytes;
+  LDS_AS uint8_t *stage1 = smem + kPageBytes + kF8PageBytes;
+  volatile LDS_AS int *rerun_flag = (volatile LDS_AS int *)(smem + 2 * kPageBytes);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int seg = blockIdx.x;                         // one split of one sequence
+  const int rt = blockIdx.y % a.row_tiles;
+  const int hk = blockIdx.y / a.row_tiles;
+  const int32_t *md = a.tile_md + (long)seg * 8;
+  const int b = md[0];
+  if (b < 0 || b >= a.batch) return;                  // unused row of the table
+  const int nsplit = md[4];
+  // Lengths and page ranges are clamped so that every global address below
+  // stays inside its buffer whatever the table or cache_seqlens hold.
+  const int L = max(0, min(a.seqlens[b], a.max_blocks * kPage));
+  const int nblk = (L + kPage - 1) / kPage;
+  const int lo = max(0, md[1]);
+  const int hi = min(md[2], nblk);
+  if (tid == 0) *rerun_flag = 0;
+
+  const int wrow0 = rt * kRowsPerTile + wave * 32;
+  const bool active = wrow0 < a.rows;                 // wave-uniform
+  const int row = wrow0 + (lane & 31);
+  const bool row_ok = row < a.rows;
+  const int qi = row / a.group;                       // query token of this row
+  const int h = hk * a.group + (row - qi * a.group);  // query head of this row
+  const int rowc = min(row, a.rows - 1);
+  const int qic = rowc / a.group;
+  const int hc = hk * a.group + (rowc - qic * a.group);
+  const int hl = lane >> 5;
+  const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + qi)) : L;
+
+  const int elem = kFp8 ? 1 : 2;
+  const int tok_stride = a.hk * kHeadDim * elem;
+  const long page_stride = (long)kPage * tok_stride;
+  const uint8_t *kv_head = a.kv + (long)hk * kHeadDim * elem;
+  const int32_t *bt = a.block_table + (long)b * a.max_blocks;
+
+  float m = kNegInf, l = 0.f, m_restart = kNegInf;
+  // O^T accumulators start as the result of an all-zero MFMA so that they
+  // live in accumulation registers from the first page on.
+  f32x16 o[kOTiles];
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+
+  if (hi > lo) {
+    bf16x8 qf[kKSteps];
+    // Rows past `rows` load a valid row instead (their results are never written).
+    const uint16_t *qrow = a.q + (((long)b * a.s_q + qic) * a.hq + hc) * kHeadDim + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+
+    auto issue = [&](int j, LDS_AS uint8_t *dst) {
+      const int pgi = max(0, min(bt[j], a.num_blocks - 1));
+      const uint8_t *tok0 = kv_head + (long)pgi * page_stride;
+      const int nvalid = min(kPage, L - j * kPage);
+      if (kFp8) dma_page_fp8(tok0, tok_stride, nvalid, dst, wave, lane);
+      else dma_page_bf16(tok0, tok_stride, nvalid, dst, wave, lane);
+    };
+    for (int pass = 0;; ++pass) {
+      bool need = false;
+      issue(lo, kFp8 ? stage0 : page0);
+      for (int j = lo; j < hi; ++j) {
+        const int cur = (j - lo) & 1;
+        // Page j has landed in every wave's share; every wave is done with
+        // page j - 1, whose buffer the prefetch of page j + 1 reuses.
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (j + 1 < hi) issue(j + 1, kFp8 ? (cur ? stage0 : stage1) : (cur ? page0 : page1));
+        const LDS_AS uint8_t *pg;
+        if (kFp8) {
+          widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane);
+          __syncthreads();
+          pg = page0;
+        } else {
+          pg = cur ? page1 : page0;
+        }
+        if (active) need |= attend_page(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, a.scale_log2);
+      }
+      if (need && lane == 0) *rerun_flag = 1;
+      __syncthreads();
+      const bool again = (*rerun_flag != 0) && (pass + 1 < kMaxPasses);   // workgroup-uniform
+      __syncthreads();
+      if (!again) break;
+      if (tid == 0) *rerun_flag = 0;
+      if (m_restart != kNegInf) m = m_restart;
+      m_restart = kNegInf;
+      l = 0.f;
+#pragma unroll
+      for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+    }
+  }
+
+  // Epilogue: lane holds head `row`, dims 32*t + 8*(i/4) + 4*hl + i%4 of o[t][i].
+  if (active && row_ok) {
+    const bool has = l > 0.f;
+    const float inv = has ? 1.f / l : 0.f;
+    const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
+    if (nsplit <= 1) {
+      uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + 4 * hl;
+      const float f = inv * a.v_scale;
+#pragma unroll
+      for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const __bf16 v0 = (__bf16)(o[t][4 * q4 + 0] * f), v1 = (__bf16)(o[t][4 * q4 + 1] * f);
+          const __bf16 v2 = (__bf16)(o[t][4 * q4 + 2] * f), v3 = (__bf16)(o[t][4 * q4 + 3] * f);
+          *(bf16x4 *)(orow + 32 * t + 8 * q4) = bf16x4{v0, v1, v2, v3};
+        }
+      if (hl == 0) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
+    } else {
+      // Partial slot of split k of b is its table row, num_splits[b] + k.
+      const long prow = ((long)seg * a.hk + hk) * a.rows + row;
+      float *po = a.part_o + prow * kHeadDimV + 4 * hl;
+#pragma unroll
+      for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4 *)(po + 32 * t + 8 * q4) =
+              f32x4{o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv};
+      if (hl == 0) a.part_lse[prow] = lse_v;
+    }
+  }
+}
+
+// Merge the split partials of every sequence with more than one split:
+// out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
+// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
+  const int b = blockIdx.x;
+  const int nrows = a.batch + a.num_parts - 1;        // partial slots written by the decode kernel
+  const int slot0 = max(0, min(a.num_splits[b], nrows));
+  const int n = min(a.num_splits[b + 1] - slot0, nrows - slot0);
+  if (n <= 1) return;
+  const int groups = (a.rows + 3) / 4;
+  const int hk = blockIdx.y / groups;
+  const int row = (blockIdx.y - hk * groups) * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int lane = threadIdx.x & 63;
+  const long sstride = (long)a.hk * a.rows;
+  const float *pl = a.part_lse + ((long)slot0 * a.hk + hk) * a.rows + row;
+  float mu = kNegInf;
+  for (int k = 0; k < n; ++k) mu = fmaxf(mu, pl[k * sstride]);
+  f32x4 acc0 = {}, acc1 = {};
+  float Z = 0.f;
+  if (mu != kNegInf) {
+    const float *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
+    for (int k = 0; k < n; ++k) {
+      const float w = __builtin_amdgcn_exp2f((pl[k * sstride] - mu) * kLog2e);
+      Z += w;
+      const f32x4 v0 = *(const f32x4 *)(po + k * sstride * kHeadDimV);
+      const f32x4 v1 = *(const f32x4 *)(po + k * sstride * kHeadDimV + 4);
+      acc0 += w * v0;
+      acc1 += w * v1;
+    }
+  }
+  const float inv = Z > 0.f ? a.v_scale / Z : 0.f;
+  const int qi = row / a.group;
+  const int h = hk * a.group + (row - qi * a.group);
+  uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + lane * 8;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  bf16x8_t ov;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ov[e] = (__bf16)(acc0[e] * inv);
+    ov[4 + e] = (__bf16)(acc1[e] * inv);
+  }
+  *(bf16x8_t *)orow = ov;
+  if (lane == 0) a.lse[((long)b * a.hq + h) * a.s_q + qi] = Z > 0.f ? mu + __logf(Z) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  const size_t smem = 2 * (size_t)kPageBytes + 16;   // pages (or page + fp8 staging) + restart flag
+  static_assert(kPageBytes + 2 * kF8PageBytes == 2 * kPageBytes, "fp8 staging fills the second page slot");
+  const dim3 grid(a.batch + a.num_parts - 1, a.row_tiles * a.hk);
+  if (a.kv_fp8) {
+    hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(kThreads), smem, stream, a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(kThreads), smem, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid(a.batch, a.hk * ((a.rows + 3) / 4));
+  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,37 @@
+// Internal launch interface between the C-ABI layer (mla_api.cpp) and the
+// gfx950 kernels.  Not installed; the public surface is include/mla_decode.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kHeadDim = 576;
+constexpr int kHeadDimV = 512;
+constexpr int kPage = 64;
+constexpr int kRowsPerTile = 128;     // rows (query heads x s_q) per decode workgroup
+constexpr int kMetaThreads = 1024;
+
+struct DecodeArgs {
+  const uint16_t *q;          // bf16 bits [B][s_q][Hq][576]
+  const uint8_t *kv;          // [num_blocks][64][Hk][576] bf16 or e4m3fn
+  const int32_t *block_table; // [B][max_blocks]
+  const int32_t *seqlens;     // [B]
+  const int32_t *tile_md;     // [batch + num_parts - 1][8], one row per split
+  const int32_t *num_splits;  // [B+1]
+  uint16_t *out;              // bf16 bits [B][s_q][Hq][512]
+  float *lse;                 // [B][Hq][s_q]
+  float *part_o;              // [slots][Hk][M][512]
+  float *part_lse;            // [slots][Hk][M]
+  int batch, s_q, hq, hk, group, rows, max_blocks, row_tiles, num_parts, num_blocks;
+  int kv_fp8, causal;
+  float scale_log2;           // softmax_scale * log2(e)
+  float v_scale;
+};
+
+hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int fixed_cost,
+                           int32_t *tile_md, int32_t *num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,99 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/mla_decode.h declares, and rejects bad arguments on the
+host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_paged_kv_metadata_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("mla_get_metadata", "mla_decode_fwd", "mla_num_parts", "mla_workspace_bytes", "mla_status_str",
+              "mla_get_metadata_ex"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mla.load_library()
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = mla.load_library()
+    for s in range(6):
+        assert lib.mla_status_str(s)
+    assert lib.mla_status_str(0) == b"ok"
+
+
+def test_workspace_bytes():
+    n = mla.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
+    slots = 64 + 256
+    assert n >= slots * 128 * 512 * 4 + slots * 128 * 4
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_workspace_bytes(0, 1, 128, 1, 512, 256)
+    assert e.value.status == 1
+    with pytest.raises(mla.MlaError):
+        mla.mla_workspace_bytes(2, 1, 6, 4, 512, 8)      # heads not divisible
+
+
+def _decode(lib, **kw):
+    a = dict(q=1, batch=2, s_q=1, hq=16, d=576, kv=1, dt=0, nb=8, page=64, hk=1, bt=1, maxb=5, sl=1, dv=512,
+             scale=1 / 24, vs=1.0, causal=0, md=1, parts=4, ns=1, ws=1, wsb=1 << 30, out=1, lse=1, stream=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.mla_decode_fwd(P(a["q"]), a["batch"], a["s_q"], a["hq"], a["d"], P(a["kv"]), a["dt"], a["nb"],
+                              a["page"], a["hk"], P(a["bt"]), a["maxb"], P(a["sl"]), a["dv"], a["scale"],
+                              a["vs"], a["causal"], P(a["md"]), a["parts"], P(a["ns"]), P(a["ws"]), a["wsb"],
+                              P(a["out"]), P(a["lse"]), P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(out=0), 1), (dict(lse=0), 1), (dict(batch=0), 1), (dict(hq=6, hk=4), 1),
+    (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(d=192), 2), (dict(dv=128), 2),
+    (dict(page=16), 2), (dict(dt=7), 2), (dict(s_q=9, hq=128), 2), (dict(batch=9000), 2),
+    (dict(wsb=16), 3), (dict(ws=0), 3),
+])
+def test_decode_rejects_bad_arguments_before_any_device_call(kw, status):
+    # Pointers are dummies: a rejected call must never dereference or launch.
+    assert _decode(mla.load_library(), **kw) == status
+
+
+def test_metadata_rejects_bad_arguments():
+    lib = mla.load_library()
+    P = ctypes.c_void_p
+    assert lib.mla_get_metadata_ex(P(1), 0, 128, 1, 4, 2, P(1), P(1), P(0)) == 1
+    assert lib.mla_get_metadata_ex(P(1), 4, 128, 1, 0, 2, P(1), P(1), P(0)) == 1
+    assert lib.mla_get_metadata_ex(P(1), 4, 128, 1, 4, 0, P(1), P(1), P(0)) == 1
+    assert lib.mla_get_metadata_ex(P(0), 4, 128, 1, 4, 2, P(1), P(1), P(0)) == 1
+    assert lib.mla_get_metadata_ex(P(1), 9000, 128, 1, 4, 2, P(1), P(1), P(0)) == 2
+    assert lib.mla_num_parts(4, 128, 1, None) == 1
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        mla.mla_get_metadata(torch.zeros(4, dtype=torch.int32), 128, 1)
+
+
+def test_no_device_is_reported_when_arguments_are_valid():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    lib = mla.load_library()
+    assert _decode(lib) == 4
+    n = ctypes.c_int(0)
+    assert lib.mla_num_parts(4, 128, 1, ctypes.byref(n)) == 4

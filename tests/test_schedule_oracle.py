@@ -48,7 +48,9 @@ def test_single_part_takes_everything_in_one_split_each():
     L = [5, 700, 0, 64]
     md, ns = schedule(L, 1, 2)
     assert ns.tolist() == [0, 1, 2, 3, 4]
-    assert md[0, :5].tolist() == [0, 0, 3, 1, 0]
+    assert md.shape == (4, 8)
+    assert md[:, :5].tolist() == [[0, 0, 1, 0, 1], [1, 0, 11, 0, 1], [2, 0, 0, 0, 1], [3, 0, 1, 0, 1]]
+    assert (md[:, 7] == 0).all()
 
 
 def test_long_sequence_is_spread_over_many_parts():
@@ -57,22 +59,28 @@ def test_long_sequence_is_spread_over_many_parts():
     assert ns[1] - ns[0] > 100          # the 65536-token sequence is split widely
 
 
-@pytest.mark.parametrize("mutation", ["drop_page", "dup_page", "bad_rank", "bad_count", "overload"])
+@pytest.mark.parametrize("mutation", ["drop_page", "dup_page", "bad_rank", "bad_count", "overload", "part_gap",
+                                      "stray_row"])
 def test_checker_catches_planted_mistakes(mutation):
     L = [300, 129, 64, 1000]
     md, ns = schedule(L, 6, 2)
     md = md.copy()
     ns = ns.copy()
     if mutation == "drop_page":
-        md[0, 3] -= 1
+        md[0, 2] -= 1
     elif mutation == "dup_page":
         md[1, 1] -= 1
     elif mutation == "bad_rank":
-        k = next(p for p in range(6) if md[p, 4] > 0)
-        md[k, 4] += 1
+        k = next(s for s in range(len(md)) if md[s, 3] > 0)
+        md[k, 3] += 1
     elif mutation == "bad_count":
         ns[2:] += 1
     elif mutation == "overload":
         md[:, 5] = 1                      # claimed payload too small for the real costs
+    elif mutation == "part_gap":
+        k = next(s for s in range(len(md)) if md[s, 3] > 0)
+        md[k, 7] += 1
+    elif mutation == "stray_row":
+        md[-1, 0] = 2
     with pytest.raises(AssertionError):
         check_schedule(md, ns, L, 6, 2)
