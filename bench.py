@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="KV pool replicas rotated across steps")
     ap.add_argument("--num-parts", type=int, default=None, help="override the scheduler's balancing target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this decode path is built and "
@@ -91,6 +93,15 @@ def main():
     import mla_paged_kv_metadata_amd as mla
     from workloads import make_config
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return
     mla.load_library()
     dev = torch.device("cuda:0")
     w = make_config(2)

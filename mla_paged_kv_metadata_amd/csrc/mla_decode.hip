@@ -66,11 +66,17 @@ static_assert(kPage * kF8RowChunks % kThreads == 0, "fp8 page must split evenly 
 
 // LDS layout of a bf16 page: nine column groups of 8 chunks (16 B each);
 // group j holds chunks 8j..8j+7 of all 64 tokens, 128 B per token, with the
-// chunk index XOR-swizzled by token & 7.  Returns the 16-byte chunk index of
+// chunk index XOR-swizzled by h(t) = (t1, t2, t3) -> bits (2, 1, 0), t_k
+// being bit k of the token.  On the 64-bank (256 B/clock) LDS this makes
+// both operand reads conflict-free: 16 consecutive tokens reading one chunk
+// (the K operand of S^T) hit 16 distinct 16-byte bank slots, and 4
+// consecutive tokens x 4 aligned chunks (the V^T transposing reads of 32
+// lanes) hit 16 distinct slots.  Returns the 16-byte chunk index of
 // (token t, logical chunk c).  One wave-wide 1 KiB LDS-DMA store then covers
 // 8 whole tokens of one group, so every lane's global source offset is a
 // lane constant plus a wave-uniform term.
-__device__ __forceinline__ int pos_bf16(int t, int c) { return (c >> 3) * 512 + t * 8 + ((c & 7) ^ (t & 7)); }
+__device__ __forceinline__ int swz_h(int t) { return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1); }
+__device__ __forceinline__ int pos_bf16(int t, int c) { return (c >> 3) * 512 + t * 8 + ((c & 7) ^ swz_h(t)); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -79,46 +85,44 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above.
-// Wave instruction I covers group I/8, tokens 8*(I%8) .. +7.  Rows >= nvalid
-// (past the sequence end) are replaced by row nvalid-1 so that undefined
-// cache bytes never reach LDS.
-__device__ __forceinline__ void dma_page_bf16(const uint8_t *tok0, int tok_stride, int nvalid,
-                                              LDS_AS uint8_t *dst, int wave, int lane) {
+// Wave instruction I covers group I/8, tokens 8*(I%8) .. +7.  The whole page
+// is copied; rows past the sequence end are zeroed in LDS afterwards
+// (zero_tail_rows) before any wave reads them.
+__device__ __forceinline__ void dma_page_bf16(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
+                                              int lane) {
   const int lt = lane >> 3;
-  const int lane_chunk = ((lane & 7) ^ lt) * 16;
-  if (nvalid == kPage) {
-    const int lane_off = lt * tok_stride + lane_chunk;
+  // token 8*(I%8) + lt: h(token) = (lt1, lt2, (I%8)&1) -> the low bit varies with I
+  const int lane_off0 = lt * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;       // I%8 even
+  const int lane_off1 = lt * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;   // I%8 odd
 #pragma unroll
-    for (int k = 0; k < kPageLoads; ++k) {
-      const int I = wave * kPageLoads + k;
-      const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
-      __builtin_amdgcn_global_load_lds((const void *)(src + lane_off), (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPageLoads; ++k) {
-      const int I = wave * kPageLoads + k;
-      const int t = min((I & 7) * 8 + lt, nvalid - 1);
-      const uint8_t *src = tok0 + (I >> 3) * 128;
-      __builtin_amdgcn_global_load_lds((const void *)(src + t * tok_stride + lane_chunk),
-                                       (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
-    }
+  for (int k = 0; k < kPageLoads; ++k) {
+    const int I = wave * kPageLoads + k;
+    const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
+    __builtin_amdgcn_global_load_lds((const void *)(src + ((I & 1) ? lane_off1 : lane_off0)),
+                                     (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
+  }
+}
+
+// Zero rows nvalid..63 of a bf16 page in LDS (the cache rows past a
+// sequence's end may hold anything, and 0 * NaN would poison the PV product).
+__device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid, int tid) {
+  const int first = nvalid * kRowChunks;
+  for (int i = first + tid; i < kPage * kRowChunks; i += kThreads) {
+    const int t = i / kRowChunks, c = i - t * kRowChunks;
+    *(LDS_AS u32x4 *)(page + pos_bf16(t, c) * 16) = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 // HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: wave
 // instruction I covers chunks 4*(I/4) .. +3 of tokens 16*(I%4) .. +15.
-__device__ __forceinline__ void dma_page_fp8(const uint8_t *tok0, int tok_stride, int nvalid,
-                                             LDS_AS uint8_t *dst, int wave, int lane) {
-  const int lt = lane >> 2;
-  const int lane_chunk = (lane & 3) * 16;
+__device__ __forceinline__ void dma_page_fp8(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
+                                             int lane) {
+  const int lane_off = (lane >> 2) * tok_stride + (lane & 3) * 16;
 #pragma unroll
   for (int k = 0; k < kF8PageLoads; ++k) {
     const int I = wave * kF8PageLoads + k;
-    const int t = min((I & 3) * 16 + lt, nvalid - 1);
-    const uint8_t *src = tok0 + (I >> 2) * 64;
-    __builtin_amdgcn_global_load_lds((const void *)(src + t * tok_stride + lane_chunk),
-                                     (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
+    const uint8_t *src = tok0 + ((I & 3) * 16 * tok_stride + (I >> 2) * 64);
+    __builtin_amdgcn_global_load_lds((const void *)(src + lane_off), (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
   }
 }
 
@@ -129,10 +133,12 @@ __device__ __forceinline__ unsigned pack_bf16_exact(float lo, float hi) {
 
 // Widen the staged fp8 page into the bf16 page layout.  Thread (wave, lane)
 // owns staging chunks of instruction I = 4k + wave: token 16*wave + lane/4,
-// fp8 chunk 4k + lane%4 -> bf16 chunks 2c and 2c + 1 of that token.
+// fp8 chunk 4k + lane%4 -> bf16 chunks 2c and 2c + 1 of that token.  Rows
+// past the sequence end (t >= nvalid) are written as zeros.
 __device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_AS uint8_t *page, int wave,
-                                               int lane) {
+                                               int lane, int nvalid) {
   const int t = 16 * wave + (lane >> 2);
+  const bool keep = t < nvalid;
 #pragma unroll
   for (int k = 0; k < kF8PageLoads; ++k) {
     const int c = 4 * k + (lane & 3);
@@ -142,8 +148,8 @@ __device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_
     for (int i = 0; i < 4; ++i) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
       const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
-      w[2 * i] = pack_bf16_exact(lo[0], lo[1]);
-      w[2 * i + 1] = pack_bf16_exact(hi[0], hi[1]);
+      w[2 * i] = keep ? pack_bf16_exact(lo[0], lo[1]) : 0u;
+      w[2 * i + 1] = keep ? pack_bf16_exact(hi[0], hi[1]) : 0u;
     }
     *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c) * 16) = u32x4{w[0], w[1], w[2], w[3]};
     *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c + 1) * 16) = u32x4{w[4], w[5], w[6], w[7]};
@@ -186,92 +192,148 @@ __device__ __forceinline__ void mfma_qk(f32x16 &s, const bf16x8 &a, const bf16x8
 __device__ __forceinline__ void mfma_qk_drain(f32x16 &s) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s));
 }
+// Orders a second accumulator after mfma_qk_drain (whose wait states cover it).
+__device__ __forceinline__ void mfma_qk_drain_short(f32x16 &s) { asm("" : "+v"(s)); }
+
+// Exchange with lane ^ 32 through v_permlane32_swap (no LDS round trip):
+// swapping a value with itself leaves the lower-half copy in r[0] and the
+// upper-half copy in r[1] on every lane.
+__device__ __forceinline__ float max_across_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
 
 // Returns true (wave-uniform) when some row of this wave needs a re-run.
+//   scale_log2 > 0 (softmax_scale * log2 e, clamped away from 0 by the caller);
+//   mask: some key of this page may be invisible to some row of the wave.
 __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
                                             f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
-                                            int lane, int key0, int nvis, float scale_log2) {
+                                            int lane, int key0, int nvis, float scale_log2, bool mask) {
   const int hl = lane >> 5;
   const int r = lane & 31;
-  bool need_any = false;
 
-  // K operand: logical chunk 2*ks + hl of token r (+32 per half) sits at byte
-  // 8192*(ks/4) + 128*r + 16*((2*(ks%4) + hl) ^ (r & 7)) (+4096 per half):
+  // K operand: logical chunk 2*ks + hl of token r (+32 for the second 32-token
+  // tile) sits at byte 8192*(ks/4) + 128*r + 16*((2*(ks%4) + hl) ^ h(r)) (+4096):
   // four lane bases, the rest immediates.
   const LDS_AS uint8_t *kb[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) kb[v] = pg + r * 128 + ((2 * v + hl) ^ (r & 7)) * 16;
+  for (int v = 0; v < 4; ++v) kb[v] = pg + r * 128 + ((2 * v + hl) ^ swz_h(r)) * 16;
 
   // V^T operand via transposing reads: in each 16-lane group, lane i gets
   // element i%4 of the 8-byte rows loaded by lanes 4r + i/4 (r = 0..3).
-  // Lane (group g, slot 4*rr + qd) loads token 16*ks + 4*(g/2) + rr (+8 for
-  // k-slots 4..7) at dims 32*mt + 16*(g%2) + 4*qd.  With x = 4*(g/2) + rr =
-  // token & 7 and y = 2*(g%2) + qd/2, the byte offset is
-  //   8192*(mt/2) + 2048*ks + 128*x + 64*((mt%2) ^ (g/2)) + 16*(y ^ rr) + 8*(qd%2)
-  // (+1024 for k-slots 4..7), so two lane bases (even / odd mt) plus
-  // immediates address all reads.
+  // Lane (group g, slot 4*rr + qd) loads token ta = 16*ks + 4*xb + rr
+  // (xb = g/2) for k-slots 0..3 and tb = ta + 8 for k-slots 4..7, at dims
+  // 32*mt + 16*(g%2) + 4*qd, i.e. logical chunk 4*mt + y (y = 2*(g%2) + qd/2)
+  // and byte 8*(qd%2) within it.  With h(ta) = 4*t1 + 2*xb (t1 = rr/2) and
+  // h(tb) = h(ta) + 1 the byte offset is
+  //   8192*(mt/2) + 2048*ks + 128*(4*xb + rr) + 64*((mt%2) ^ t1)
+  //   + 16*(y ^ (2*xb [+1 for tb])) + 8*(qd%2) [+ 1024 for tb],
+  // so four lane bases (ta/tb x even/odd mt) plus immediates address all reads.
   const int g = lane >> 4, s16 = lane & 15, rr = s16 >> 2, qd = s16 & 3;
-  const int xb = g >> 1;
-  const int lane_ofs = (4 * xb + rr) * 128 + ((2 * (g & 1) + (qd >> 1)) ^ rr) * 16 + (qd & 1) * 8;
-  const LDS_AS uint8_t *vb_even = pg + lane_ofs + 64 * xb;
-  const LDS_AS uint8_t *vb_odd = pg + lane_ofs + 64 * (1 - xb);
+  const int xb = g >> 1, t1 = rr >> 1, y = 2 * (g & 1) + (qd >> 1);
+  const int la = (4 * xb + rr) * 128 + (y ^ (2 * xb)) * 16 + (qd & 1) * 8;
+  const int lb = (4 * xb + rr) * 128 + 1024 + (y ^ (2 * xb + 1)) * 16 + (qd & 1) * 8;
+  const LDS_AS uint8_t *va_even = pg + la + 64 * t1, *va_odd = pg + la + 64 * (1 - t1);
+  const LDS_AS uint8_t *vb_even = pg + lb + 64 * t1, *vb_odd = pg + lb + 64 * (1 - t1);
 
+  // LDS operand loads run ahead of their MFMAs (software pipeline); loads
+  // complete in order, so each MFMA waits only for its own operand.
+  auto kload = [&](int ks, int tile) -> bf16x8 {
+    return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + tile * 4096);
+  };
+  auto vload = [&](int step, bf16x4 &lo, bf16x4 &hi) {
+    const int ks = step >> 4, mt = step & 15;         // k-step of 16 tokens, 32-dim output tile
+    const int ofs = 8192 * (mt >> 1) + 2048 * ks;
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
+  };
+
+  // S^T = K Q^T for both 32-token tiles: two independent accumulation chains
+  // interleaved, so a dependent MFMA never waits on its predecessor.
+  constexpr int kPre = 2;                              // k-steps in flight (2 fragments each)
+  bf16x8 k0[kPre], k1[kPre];
 #pragma unroll
-  for (int th = 0; th < 2; ++th) {
-    // S^T half: lane holds head r, tokens 32*th + (i/4)*8 + 4*hl + i%4.
-    f32x16 s;
+  for (int i = 0; i < kPre; ++i) {
+    k0[i] = kload(i, 0);
+    k1[i] = kload(i, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s0, s1;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 ak = *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + th * 4096);
-      if (ks == 0) mfma_qk_first(s, ak, qf[ks]);
-      else mfma_qk(s, ak, qf[ks]);
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    const int sl = ks % kPre;
+    if (ks == 0) {
+      mfma_qk_first(s0, k0[sl], qf[0]);
+      mfma_qk_first(s1, k1[sl], qf[0]);
+    } else {
+      mfma_qk(s0, k0[sl], qf[ks]);
+      mfma_qk(s1, k1[sl], qf[ks]);
     }
-    mfma_qk_drain(s);
-    float x[16];
-    float mx = kNegInf;
+    if (ks + kPre < kKSteps) {
+      k0[sl] = kload(ks + kPre, 0);
+      k1[sl] = kload(ks + kPre, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);                 // keep loads kPre k-steps ahead
+  }
+  // First V^T operands load while the softmax runs.
+  constexpr int kVPre = 4;
+  bf16x4 vlo[kVPre], vhi[kVPre];
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) vload(i, vlo[i], vhi[i]);
+  mfma_qk_drain(s0);
+  mfma_qk_drain_short(s1);
+
+  // Online softmax over this page's 64 keys: lane holds head r, tokens
+  // (i/4)*8 + 4*hl + i%4 of tile 0 (s0[i]) and 32 + the same of tile 1 (s1[i]).
+  if (mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      x[i] = s[i] * scale_log2;
-      if (key0 + 32 * th + (i >> 2) * 8 + hl * 4 + (i & 3) >= nvis) x[i] = kNegInf;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (m == kNegInf) m = mx;                       // first visible keys fix the reference
-    const bool need = mx > m + kRefSlackLog2;
-    if (need) m_restart = fmaxf(m_restart, mx);
-    need_any |= need;
-    const float mu = (m == kNegInf) ? 0.f : m;
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i] - mu);
-      ps += x[i];
-    }
-    ps += __shfl_xor(ps, 32);
-    l += ps;
-
-    // P^T operand for k-step 2*th + k: score registers 8*k .. 8*k+7.
-    bf16x8 pb[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[k][e] = (__bf16)x[8 * k + e];
-
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int ks = 2 * th + k;
-#pragma unroll
-      for (int mt = 0; mt < kOTiles; ++mt) {
-        const LDS_AS uint8_t *vb = (mt & 1) ? vb_odd : vb_even;
-        const int ofs = 8192 * (mt >> 1) + 2048 * ks;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + ofs));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + ofs + 1024));
-        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[k], o[mt], 0, 0, 0);
-      }
+      const int tok = key0 + (i >> 2) * 8 + hl * 4 + (i & 3);
+      if (tok >= nvis) s0[i] = kNegInf;
+      if (tok + 32 >= nvis) s1[i] = kNegInf;
     }
   }
-  return __ballot(need_any) != 0;
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  mx = max_across_halves(mx);
+  mx = (mx == kNegInf) ? kNegInf : mx * scale_log2;
+  if (m == kNegInf) m = mx;                           // first visible keys fix the reference
+  const bool need = mx > m + kRefSlackLog2;
+  if (need) m_restart = fmaxf(m_restart, mx);
+  const float mu = (m == kNegInf) ? 0.f : m;
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], scale_log2, -mu));
+    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], scale_log2, -mu));
+    ps += s0[i] + s1[i];
+  }
+  l += sum_across_halves(ps);
+
+  // P^T operand for k-step ks: tile ks/2, score registers 8*(ks%2) .. +7.
+  bf16x8 pb[4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pb[0][e] = (__bf16)s0[e];
+    pb[1][e] = (__bf16)s0[8 + e];
+    pb[2][e] = (__bf16)s1[e];
+    pb[3][e] = (__bf16)s1[8 + e];
+  }
+
+  // O^T += V^T P^T over 4 k-steps x 16 dim tiles.
+#pragma unroll
+  for (int step = 0; step < 4 * kOTiles; ++step) {
+    const int sl = step % kVPre;
+    const bf16x8 av = __builtin_shufflevector(vlo[sl], vhi[sl], 0, 1, 2, 3, 4, 5, 6, 7);
+    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[step >> 4], o[step & 15], 0, 0, 0);
+    if (step + kVPre < 4 * kOTiles) vload(step + kVPre, vlo[sl], vhi[sl]);
+  }
+  return __ballot(need) != 0;
 }
 
 // Number of passes a segment may take when a score overshoots the reference
@@ -319,6 +381,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int hc = hk * a.group + (rowc - qic * a.group);
   const int hl = lane >> 5;
   const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + qi)) : L;
+  // Smallest visible-key count of the workgroup (row qi = 0 of a causal tile
+  // sees the fewest keys): pages at or past it need per-key masking.
+  const int nvis_min = a.causal ? max(0, min(L, L - a.s_q + 1 + (rt * kRowsPerTile) / a.group)) : L;
+  const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
 
   const int elem = kFp8 ? 1 : 2;
   const int tok_stride = a.hk * kHeadDim * elem;
@@ -340,12 +406,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 
+    // Block-table entries of the segment live in one VGPR, lane i holding the
+    // page index of j = bt_base + i, so a page lookup is a v_readlane instead
+    // of a global-memory round trip per page; refilled every 64 pages.
+    int bt_base = lo;
+    int bt_vec = bt[min(lo + lane, nblk - 1)];
+    auto page_of = [&](int j) -> int {
+      if ((unsigned)(j - bt_base) >= 64u) {        // uniform; also on a re-run from lo
+        bt_base = j;
+        bt_vec = bt[min(j + lane, nblk - 1)];
+      }
+      return __builtin_amdgcn_readlane(bt_vec, j - bt_base);
+    };
     auto issue = [&](int j, LDS_AS uint8_t *dst) {
-      const int pgi = max(0, min(bt[j], a.num_blocks - 1));
+      const int pgi = max(0, min(page_of(j), a.num_blocks - 1));
       const uint8_t *tok0 = kv_head + (long)pgi * page_stride;
-      const int nvalid = min(kPage, L - j * kPage);
-      if (kFp8) dma_page_fp8(tok0, tok_stride, nvalid, dst, wave, lane);
-      else dma_page_bf16(tok0, tok_stride, nvalid, dst, wave, lane);
+      if (kFp8) dma_page_fp8(tok0, tok_stride, dst, wave, lane);
+      else dma_page_bf16(tok0, tok_stride, dst, wave, lane);
     };
     for (int pass = 0;; ++pass) {
       bool need = false;
@@ -356,16 +433,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         // page j - 1, whose buffer the prefetch of page j + 1 reuses.
         wait_vmcnt<0>();
         __syncthreads();
+        const int nvalid = min(kPage, L - j * kPage);
+        if (!kFp8 && nvalid < kPage) {            // the sequence's last, partial page
+          zero_tail_rows(cur ? page1 : page0, nvalid, tid);
+          __syncthreads();
+        }
         if (j + 1 < hi) issue(j + 1, kFp8 ? (cur ? stage0 : stage1) : (cur ? page0 : page1));
         const LDS_AS uint8_t *pg;
         if (kFp8) {
-          widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane);
+          widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane, nvalid);
           __syncthreads();
           pg = page0;
         } else {
           pg = cur ? page1 : page0;
         }
-        if (active) need |= attend_page(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, a.scale_log2);
+        if (active)
+          need |= attend_page(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2, (j + 1) * kPage > nvis_min);
       }
       if (need && lane == 0) *rerun_flag = 1;
       __syncthreads();
