@@ -116,7 +116,7 @@ def main():
     sl = torch.from_numpy(w.cache_seqlens).to(dev)
     hpk = w.heads_per_head_k
     P = args.num_parts or mla.mla_num_parts(w.batch, hpk, w.num_heads_k)
-    md = torch.empty((w.batch + P - 1, 8), dtype=torch.int32, device=dev)
+    md = torch.empty((P, 8), dtype=torch.int32, device=dev)
     ns = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
     out = torch.empty((w.batch, w.s_q, w.num_heads_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.num_heads_q, w.s_q), dtype=torch.float32, device=dev)

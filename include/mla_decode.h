@@ -74,8 +74,8 @@ enum mla_kv_dtype {
 const char *mla_status_str(int status);
 
 /* Host only.  Recommended balancing target (parts) for this head layout on
- * the current device: about one workgroup per compute unit, divided among the
- * row tiles and KV heads.  The tile table then has batch + num_parts - 1 rows.
+ * the current device: one persistent workgroup per compute unit, divided
+ * among the row tiles and KV heads.  The tile table has num_parts rows.
  *   heads_per_head_k = s_q * num_heads_q / num_heads_k  (FlashMLA interface
  *   page, get_mla_metadata: num_heads_per_head_k).
  * Writes *num_parts; returns MLA_OK, INVALID_ARG, NO_DEVICE or UNSUPPORTED. */
@@ -89,15 +89,18 @@ int mla_num_parts(int batch, int heads_per_head_k, int num_heads_k, int *num_par
  *   num_parts     : balancing target P >= 1, the number of equal-cost parts
  *                   the work is cut into (mla_num_parts gives the recommended
  *                   one); mla_decode_fwd must get the same value.
- *   tile_md       : device int32[(batch + num_parts - 1) * MLA_TILE_MD_INTS],
- *                   written; one row per split (the most splits possible is
- *                   batch + num_parts - 1).
+ *   tile_md       : device int32[num_parts * MLA_TILE_MD_INTS], written; one
+ *                   row per part.
  *   num_splits    : device int32[batch + 1], written: an exclusive prefix
  *                   sum, num_splits[0] = 0 and num_splits[b+1]-num_splits[b]
- *                   >= 1 is the number of splits of sequence b.
- * Row num_splits[b] + k of tile_md describes split k of sequence b:
- * [b, first page, end page (exclusive), k, splits of b, payload W,
- * fixed_cost, part]; rows past the last split hold b = -1.
+ *                   >= 1 is the number of splits of sequence b (at most
+ *                   batch + num_parts - 1 splits in all).
+ * Part p works on a run of consecutive sequences b0..b1; row p of tile_md is
+ * [b0, first page of b0, b1, end page of b1 (exclusive), split index k of
+ * b0's piece, payload W, fixed_cost, number of splits of the part]; the
+ * sequences strictly between b0 and b1 are whole, and b1's piece (when
+ * b1 > b0) starts at page 0 and is its split 0.  An idle part has
+ * b0 = b1 = -1.  Split k of sequence b is partial slot num_splits[b] + k.
  * The table depends only on cache_seqlens, the head layout and num_parts, so
  * one call serves every layer of a decode step.  No device-to-host
  * synchronisation happens. */
@@ -112,9 +115,9 @@ int mla_get_metadata(const int32_t *cache_seqlens, int batch, int heads_per_head
 int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int heads_per_head_k, int num_heads_k,
                         int num_parts, int fixed_cost, int32_t *tile_md, int32_t *num_splits, void *stream);
 
-/* Host only.  Bytes of split workspace mla_decode_fwd needs (fp32 partial
- * outputs and log-sum-exps of up to batch + num_parts - 1 splits), written
- * to *bytes.  Returns MLA_OK or INVALID_ARG. */
+/* Host only.  Bytes of split workspace mla_decode_fwd needs (bf16 partial
+ * outputs and fp32 log-sum-exps of up to batch + num_parts - 1 splits),
+ * written to *bytes.  Returns MLA_OK or INVALID_ARG. */
 int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, int head_dim_v, int num_parts,
                         size_t *bytes);
 
@@ -133,16 +136,18 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
  *                  would need a device read).  Cache rows past
  *                  cache_seqlens[b] in a sequence's last block are never read.
  *   cache_seqlens: device int32 [batch], 0 <= L_b <= max_blocks_per_seq * 64.
- *   softmax_scale: factor on q.k before the softmax (bmm1_scale for an fp8
- *                  cache).  The Python wrapper supplies 1/sqrt(head_dim) when
- *                  the caller gives none, as the pages' wrappers do.
+ *   softmax_scale: factor >= 0 on q.k before the softmax (bmm1_scale for an
+ *                  fp8 cache; a negative value is UNSUPPORTED).  The Python
+ *                  wrapper supplies 1/sqrt(head_dim) when the caller gives
+ *                  none, as the pages' wrappers do.
  *   v_scale      : factor on the weighted sum of V (bmm2_scale; 1 for bf16).
  *   causal       : 0 or 1.  Query i of s_q sees keys t < L_b - s_q + 1 + i
  *                  (bottom-right alignment).  A row with no visible key gets
  *                  out = 0 and lse = -inf.
  *   tile_md, num_parts, num_splits: from mla_get_metadata for these
- *                  cache_seqlens and this head layout (tile_md has
- *                  batch + num_parts - 1 rows).
+ *                  cache_seqlens and this head layout (tile_md has num_parts
+ *                  rows; one persistent workgroup per part and 128-row tile
+ *                  of each KV head walks its row's run of sequences).
  *   workspace    : device buffer of >= mla_workspace_bytes(...) bytes,
  *                  contents ignored on entry.
  *   out          : device bf16 [batch][s_q][num_heads_q][head_dim_v], written.
@@ -162,9 +167,9 @@ int mla_decode_fwd(const void *q, int batch, int s_q, int num_heads_q, int head_
 /* The two stages of mla_decode_fwd, for callers that time or overlap them
  * (same arguments and validation as mla_decode_fwd).
  *   mla_decode_splits : attention over every split of the tile table; writes
- *                       out / lse of sequences with one split and the fp32
- *                       partials (normalised output and log-sum-exp) of the
- *                       others into the workspace.
+ *                       out / lse of sequences with one split and the
+ *                       partials (bf16 normalised output, fp32 log-sum-exp)
+ *                       of the others into the workspace.
  *   mla_combine_splits: merges the partials of sequences with more than one
  *                       split by their log-sum-exps into out / lse.  Must run
  *                       after mla_decode_splits with the same arguments. */

@@ -101,7 +101,7 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None):
 
 
 def mla_num_parts(batch: int, heads_per_head_k: int, num_heads_k: int) -> int:
-    """Recommended rows of the tile-scheduler table on the current device."""
+    """Recommended number of parts (rows of the tile-scheduler table) on the current device."""
     n = _c_int(0)
     _check(load_library().mla_num_parts(batch, heads_per_head_k, num_heads_k, ctypes.byref(n)))
     return n.value
@@ -116,9 +116,9 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, num_heads_per_head_k: int, num
     cache_seqlens: (batch,) int32 on the GPU.  num_heads_per_head_k =
     seq_len_q * num_heads_q // num_heads_k.  num_parts is the balancing
     target (default: about one workgroup per compute unit).  Returns
-    (tile_scheduler_metadata (batch + num_parts - 1, 8) int32, one row per
-    split, num_splits (batch + 1) int32), computed by the scheduler kernel on
-    the current stream.
+    (tile_scheduler_metadata (num_parts, 8) int32, one row per part,
+    num_splits (batch + 1) int32), computed by the scheduler kernel on the
+    current stream.
     """
     lib = load_library()
     _need(cache_seqlens, "cache_seqlens", torch.int32)
@@ -131,13 +131,13 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, num_heads_per_head_k: int, num
             num_parts = mla_num_parts(B, num_heads_per_head_k, num_heads_k)
         md, ns = tile_md, num_splits
         if md is None:
-            md = torch.empty((B + num_parts - 1, TILE_MD_INTS), dtype=torch.int32, device=dev)
+            md = torch.empty((num_parts, TILE_MD_INTS), dtype=torch.int32, device=dev)
         if ns is None:
             ns = torch.empty((B + 1,), dtype=torch.int32, device=dev)
         _need(md, "tile_md", torch.int32, dev)
         _need(ns, "num_splits", torch.int32, dev)
-        if tuple(md.shape) != (B + num_parts - 1, TILE_MD_INTS) or tuple(ns.shape) != (B + 1,):
-            raise ValueError("tile_md must be (batch + num_parts - 1, 8) and num_splits (batch + 1,)")
+        if tuple(md.shape) != (num_parts, TILE_MD_INTS) or tuple(ns.shape) != (B + 1,):
+            raise ValueError("tile_md must be (num_parts, 8) and num_splits (batch + 1,)")
         if fixed_cost is None:
             rc = lib.mla_get_metadata(_ptr(cache_seqlens), B, num_heads_per_head_k, num_heads_k, _ptr(md),
                                       num_parts, _ptr(ns), _stream(dev))
@@ -212,11 +212,11 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
     if cache_seqlens.shape != (B,):
         raise ValueError("cache_seqlens must be (batch,)")
     if (tile_scheduler_metadata.dim() != 2 or tile_scheduler_metadata.shape[1] != TILE_MD_INTS
-            or tile_scheduler_metadata.shape[0] < B):
-        raise ValueError("tile_scheduler_metadata must be (batch + num_parts - 1, 8)")
+            or tile_scheduler_metadata.shape[0] < 1):
+        raise ValueError("tile_scheduler_metadata must be (num_parts, 8)")
     if num_splits.shape != (B + 1,):
         raise ValueError("num_splits must be (batch + 1,)")
-    num_parts = tile_scheduler_metadata.shape[0] - B + 1
+    num_parts = tile_scheduler_metadata.shape[0]
     if out is None:
         out = torch.empty((B, s_q, Hq, head_dim_v), dtype=torch.bfloat16, device=dev)
     else:

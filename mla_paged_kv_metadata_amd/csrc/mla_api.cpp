@@ -66,10 +66,10 @@ int check_heads(int batch, int heads_per_head_k, int num_heads_k) {
 int row_tiles(int rows) { return (rows + mla::kRowsPerTile - 1) / mla::kRowsPerTile; }
 
 // Per-split overhead in page units: loading the rows' q (rows x 1152 B) and
-// writing plus re-reading an fp32 partial (rows x 2 x 2052 B), against a
-// 73728-byte bf16 page.
+// writing plus re-reading a bf16 partial with its lse (rows x 2 x 1028 B),
+// against a 73728-byte bf16 page.
 int default_fixed_cost(int rows) {
-  const long bytes = (long)rows * (1152 + 2 * 2052);
+  const long bytes = (long)rows * (1152 + 2 * 1028);
   return (int)std::max(1L, (bytes + 36864) / 73728);
 }
 
@@ -134,7 +134,7 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
   if (num_heads_q % num_heads_k) return fail(MLA_ERR_INVALID_ARG, "num_heads_q must be a multiple of num_heads_k");
   const size_t slots = (size_t)batch + (size_t)num_parts;
   const size_t rows = (size_t)s_q * (num_heads_q / num_heads_k) * num_heads_k;
-  *bytes = align256(slots * rows * head_dim_v * sizeof(float)) + align256(slots * rows * sizeof(float));
+  *bytes = align256(slots * rows * head_dim_v * sizeof(uint16_t)) + align256(slots * rows * sizeof(float));
   return MLA_OK;
 }
 
@@ -158,6 +158,7 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (!std::isfinite(softmax_scale) || !std::isfinite(v_scale))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale and v_scale must be finite");
+  if (softmax_scale < 0.f) return fail(MLA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (head_dim != MLA_HEAD_DIM) return fail(MLA_ERR_UNSUPPORTED, "head_dim must be 576 (512 latent + 64 rope)");
   if (head_dim_v != MLA_HEAD_DIM_V) return fail(MLA_ERR_UNSUPPORTED, "head_dim_v must be 512");
   if (page_block_size != MLA_PAGE_BLOCK_SIZE) return fail(MLA_ERR_UNSUPPORTED, "page_block_size must be 64");
@@ -184,8 +185,8 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   a.out = (uint16_t *)out;
   a.lse = lse;
   const size_t slots = (size_t)batch + (size_t)num_parts;
-  a.part_o = (float *)workspace;
-  a.part_lse = (float *)((char *)workspace + align256(slots * rows * num_heads_k * head_dim_v * sizeof(float)));
+  a.part_o = (uint16_t *)workspace;
+  a.part_lse = (float *)((char *)workspace + align256(slots * rows * num_heads_k * head_dim_v * sizeof(uint16_t)));
   a.batch = batch;
   a.s_q = s_q;
   a.hq = num_heads_q;

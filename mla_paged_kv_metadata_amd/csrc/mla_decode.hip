@@ -84,23 +84,37 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above.
-// Wave instruction I covers group I/8, tokens 8*(I%8) .. +7.  The whole page
-// is copied; rows past the sequence end are zeroed in LDS afterwards
-// (zero_tail_rows) before any wave reads them.
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's
+// 16 bytes land at lds + 16 * i.  Written as inline assembly on purpose: the
+// compiler cannot tell which LDS bytes a copy writes, so for its own copy
+// intrinsic it waits for every copy in flight before any later transposing
+// LDS read -- which would serialise the next page's copy with this page's PV
+// product.  Completion is instead awaited explicitly (wait_vmcnt) before the
+// barrier that publishes a page.  M0 holds the LDS base; an M0 write needs
+// one wait state before an LDS-DMA instruction.
+__device__ __forceinline__ void lds_dma16(const void *src, LDS_AS void *lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "m0");
+}
+
+// HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above,
+// as kPageLoads wave instructions per wave.  Wave instruction I covers group
+// I/8, tokens 8*(I%8) .. +7.  The whole page is copied; rows past the
+// sequence end are zeroed in LDS afterwards (zero_tail_rows) before any wave
+// reads them.  dma_bf16_step issues instruction k of this wave.
+__device__ __forceinline__ void dma_bf16_step(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
+                                              int lane, int k) {
+  const int lt = lane >> 3;
+  const int I = wave * kPageLoads + k;
+  // token 8*(I%8) + lt: h(token) = (lt1, lt2, (I%8)&1) -> the low bit varies with I
+  const int lane_off = lt * tok_stride + ((lane & 7) ^ swz_h(lt + 8 * (I & 1))) * 16;
+  const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
+  lds_dma16(src + lane_off, dst + I * 1024);
+}
 __device__ __forceinline__ void dma_page_bf16(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
                                               int lane) {
-  const int lt = lane >> 3;
-  // token 8*(I%8) + lt: h(token) = (lt1, lt2, (I%8)&1) -> the low bit varies with I
-  const int lane_off0 = lt * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;       // I%8 even
-  const int lane_off1 = lt * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;   // I%8 odd
 #pragma unroll
-  for (int k = 0; k < kPageLoads; ++k) {
-    const int I = wave * kPageLoads + k;
-    const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
-    __builtin_amdgcn_global_load_lds((const void *)(src + ((I & 1) ? lane_off1 : lane_off0)),
-                                     (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
-  }
+  for (int k = 0; k < kPageLoads; ++k) dma_bf16_step(tok0, tok_stride, dst, wave, lane, k);
 }
 
 // Zero rows nvalid..63 of a bf16 page in LDS (the cache rows past a
@@ -115,15 +129,17 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid,
 
 // HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: wave
 // instruction I covers chunks 4*(I/4) .. +3 of tokens 16*(I%4) .. +15.
+__device__ __forceinline__ void dma_fp8_step(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
+                                             int lane, int k) {
+  const int lane_off = (lane >> 2) * tok_stride + (lane & 3) * 16;
+  const int I = wave * kF8PageLoads + k;
+  const uint8_t *src = tok0 + ((I & 3) * 16 * tok_stride + (I >> 2) * 64);
+  lds_dma16(src + lane_off, dst + I * 1024);
+}
 __device__ __forceinline__ void dma_page_fp8(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
                                              int lane) {
-  const int lane_off = (lane >> 2) * tok_stride + (lane & 3) * 16;
 #pragma unroll
-  for (int k = 0; k < kF8PageLoads; ++k) {
-    const int I = wave * kF8PageLoads + k;
-    const uint8_t *src = tok0 + ((I & 3) * 16 * tok_stride + (I >> 2) * 64);
-    __builtin_amdgcn_global_load_lds((const void *)(src + lane_off), (LDS_AS void *)(dst + I * 1024), 16, 0, 0);
-  }
+  for (int k = 0; k < kF8PageLoads; ++k) dma_fp8_step(tok0, tok_stride, dst, wave, lane, k);
 }
 
 // Two floats that hold bf16-exact values -> packed bf16 pair (truncation is exact here).
@@ -207,12 +223,26 @@ __device__ __forceinline__ float sum_across_halves(float v) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// Where the next page's HBM -> LDS copy goes; its wave instructions are
+// spread over the first k-steps of this page's S^T product instead of being
+// issued in one burst, so the wave keeps feeding the matrix core while the
+// address unit drains them.
+struct NextPage {
+  const uint8_t *tok0;        // cache row of the next page's first token (this KV head)
+  LDS_AS uint8_t *dst;        // its LDS (bf16 page or fp8 staging) buffer
+  int tok_stride;
+  int wave;
+  bool valid;                 // workgroup-uniform
+};
+
 // Returns true (wave-uniform) when some row of this wave needs a re-run.
 //   scale_log2 > 0 (softmax_scale * log2 e, clamped away from 0 by the caller);
 //   mask: some key of this page may be invisible to some row of the wave.
+template <bool kFp8>
 __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
                                             f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
-                                            int lane, int key0, int nvis, float scale_log2, bool mask) {
+                                            int lane, int key0, int nvis, float scale_log2, bool mask,
+                                            const NextPage &nx) {
   const int hl = lane >> 5;
   const int r = lane & 31;
 
@@ -276,6 +306,10 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
     if (ks + kPre < kKSteps) {
       k0[sl] = kload(ks + kPre, 0);
       k1[sl] = kload(ks + kPre, 1);
+    }
+    if (nx.valid && ks < (kFp8 ? kF8PageLoads : kPageLoads)) {
+      if (kFp8) dma_fp8_step(nx.tok0, nx.tok_stride, nx.dst, nx.wave, lane, ks);
+      else dma_bf16_step(nx.tok0, nx.tok_stride, nx.dst, nx.wave, lane, ks);
     }
     __builtin_amdgcn_sched_barrier(0);                 // keep loads kPre k-steps ahead
   }
@@ -355,20 +389,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int seg = blockIdx.x;                         // one split of one sequence
   const int rt = blockIdx.y % a.row_tiles;
   const int hk = blockIdx.y / a.row_tiles;
-  const int32_t *md = a.tile_md + (long)seg * 8;
-  const int b = md[0];
-  if (b < 0 || b >= a.batch) return;                  // unused row of the table
-  const int nsplit = md[4];
-  // Lengths and page ranges are clamped so that every global address below
-  // stays inside its buffer whatever the table or cache_seqlens hold.
-  const int L = max(0, min(a.seqlens[b], a.max_blocks * kPage));
-  const int nblk = (L + kPage - 1) / kPage;
-  const int lo = max(0, md[1]);
-  const int hi = min(md[2], nblk);
-  if (tid == 0) *rerun_flag = 0;
+  // Table row of this part: a run of sequences b0..b1, the first and last
+  // possibly cut at a page boundary.
+  const int32_t *md = a.tile_md + (long)blockIdx.x * 8;
+  const int b0 = md[0];
+  if (b0 < 0 || b0 >= a.batch) return;                // idle part
+  const int b1 = min(max(md[2], b0), a.batch - 1);
+  const int nslots = a.batch + a.num_parts - 1;       // partial slots in the workspace
 
   const int wrow0 = rt * kRowsPerTile + wave * 32;
   const bool active = wrow0 < a.rows;                 // wave-uniform
@@ -380,118 +409,138 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int qic = rowc / a.group;
   const int hc = hk * a.group + (rowc - qic * a.group);
   const int hl = lane >> 5;
-  const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + qi)) : L;
-  // Smallest visible-key count of the workgroup (row qi = 0 of a causal tile
-  // sees the fewest keys): pages at or past it need per-key masking.
-  const int nvis_min = a.causal ? max(0, min(L, L - a.s_q + 1 + (rt * kRowsPerTile) / a.group)) : L;
+  const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
 
   const int elem = kFp8 ? 1 : 2;
   const int tok_stride = a.hk * kHeadDim * elem;
   const long page_stride = (long)kPage * tok_stride;
   const uint8_t *kv_head = a.kv + (long)hk * kHeadDim * elem;
-  const int32_t *bt = a.block_table + (long)b * a.max_blocks;
 
-  float m = kNegInf, l = 0.f, m_restart = kNegInf;
-  // O^T accumulators start as the result of an all-zero MFMA so that they
-  // live in accumulation registers from the first page on.
-  f32x16 o[kOTiles];
+  for (int b = b0; b <= b1; ++b) {
+    // Lengths, page ranges and slots are clamped so that every global address
+    // below stays inside its buffer whatever the table or cache_seqlens hold.
+    const int L = max(0, min(a.seqlens[b], a.max_blocks * kPage));
+    const int nblk = (L + kPage - 1) / kPage;
+    const int hi = b == b1 ? max(0, min(md[3], nblk)) : nblk;
+    const int lo = b == b0 ? max(0, min(md[1], hi)) : 0;
+    const int first_slot = a.num_splits[b];
+    const int nsplit = a.num_splits[b + 1] - first_slot;
+    const int slot = max(0, min(first_slot + (b == b0 ? md[4] : 0), nslots - 1));
+    const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + qi)) : L;
+    // Smallest visible-key count of the workgroup (its first query token sees
+    // the fewest keys): pages at or past it need per-key masking.
+    const int nvis_min = a.causal ? max(0, min(L, L - a.s_q + 1 + qi_min)) : L;
+    const int32_t *bt = a.block_table + (long)b * a.max_blocks;
+    if (tid == 0) *rerun_flag = 0;
+
+    float m = kNegInf, l = 0.f, m_restart = kNegInf;
+    // O^T accumulators start as the result of an all-zero MFMA so that they
+    // live in accumulation registers from the first page on.
+    f32x16 o[kOTiles];
 #pragma unroll
-  for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+    for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
 
-  if (hi > lo) {
-    bf16x8 qf[kKSteps];
-    // Rows past `rows` load a valid row instead (their results are never written).
-    const uint16_t *qrow = a.q + (((long)b * a.s_q + qic) * a.hq + hc) * kHeadDim + 8 * hl;
+    if (hi > lo) {
+      bf16x8 qf[kKSteps];
+      // Rows past `rows` load a valid row instead (their results are never written).
+      const uint16_t *qrow = a.q + (((long)b * a.s_q + qic) * a.hq + hc) * kHeadDim + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 
-    // Block-table entries of the segment live in one VGPR, lane i holding the
-    // page index of j = bt_base + i, so a page lookup is a v_readlane instead
-    // of a global-memory round trip per page; refilled every 64 pages.
-    int bt_base = lo;
-    int bt_vec = bt[min(lo + lane, nblk - 1)];
-    auto page_of = [&](int j) -> int {
-      if ((unsigned)(j - bt_base) >= 64u) {        // uniform; also on a re-run from lo
-        bt_base = j;
-        bt_vec = bt[min(j + lane, nblk - 1)];
-      }
-      return __builtin_amdgcn_readlane(bt_vec, j - bt_base);
-    };
-    auto issue = [&](int j, LDS_AS uint8_t *dst) {
-      const int pgi = max(0, min(page_of(j), a.num_blocks - 1));
-      const uint8_t *tok0 = kv_head + (long)pgi * page_stride;
-      if (kFp8) dma_page_fp8(tok0, tok_stride, dst, wave, lane);
-      else dma_page_bf16(tok0, tok_stride, dst, wave, lane);
-    };
-    for (int pass = 0;; ++pass) {
-      bool need = false;
-      issue(lo, kFp8 ? stage0 : page0);
-      for (int j = lo; j < hi; ++j) {
-        const int cur = (j - lo) & 1;
-        // Page j has landed in every wave's share; every wave is done with
-        // page j - 1, whose buffer the prefetch of page j + 1 reuses.
-        wait_vmcnt<0>();
+      // Block-table entries of the split live in one VGPR, lane i holding the
+      // page index of j = bt_base + i, so a page lookup is a v_readlane instead
+      // of a global-memory round trip per page; refilled every 64 pages.
+      int bt_base = lo;
+      int bt_vec = bt[min(lo + lane, nblk - 1)];
+      auto page_of = [&](int j) -> int {
+        if ((unsigned)(j - bt_base) >= 64u) {        // uniform; also on a re-run from lo
+          bt_base = j;
+          bt_vec = bt[min(j + lane, nblk - 1)];
+        }
+        return __builtin_amdgcn_readlane(bt_vec, j - bt_base);
+      };
+      auto page_src = [&](int j) -> const uint8_t * {
+        const int pgi = max(0, min(page_of(j), a.num_blocks - 1));
+        return kv_head + (long)pgi * page_stride;
+      };
+      for (int pass = 0;; ++pass) {
+        bool need = false;
+        if (kFp8) dma_page_fp8(page_src(lo), tok_stride, stage0, wave, lane);
+        else dma_page_bf16(page_src(lo), tok_stride, page0, wave, lane);
+        for (int j = lo; j < hi; ++j) {
+          const int cur = (j - lo) & 1;
+          // Page j has landed in every wave's share; every wave is done with
+          // page j - 1, whose buffer the copy of page j + 1 reuses.
+          wait_vmcnt<0>();
+          __syncthreads();
+          const int nvalid = min(kPage, L - j * kPage);
+          if (!kFp8 && nvalid < kPage) {            // the sequence's last, partial page
+            zero_tail_rows(cur ? page1 : page0, nvalid, tid);
+            __syncthreads();
+          }
+          NextPage nx;
+          nx.valid = j + 1 < hi;
+          nx.tok0 = nx.valid ? page_src(j + 1) : kv_head;
+          nx.dst = kFp8 ? (cur ? stage0 : stage1) : (cur ? page0 : page1);
+          nx.tok_stride = tok_stride;
+          nx.wave = wave;
+          const LDS_AS uint8_t *pg;
+          if (kFp8) {
+            widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane, nvalid);
+            __syncthreads();
+            pg = page0;
+          } else {
+            pg = cur ? page1 : page0;
+          }
+          if (active) {
+            need |= attend_page<kFp8>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
+                                      (j + 1) * kPage > nvis_min, nx);
+          } else if (nx.valid) {                    // a wave without rows still copies its share
+            if (kFp8) dma_page_fp8(nx.tok0, tok_stride, nx.dst, wave, lane);
+            else dma_page_bf16(nx.tok0, tok_stride, nx.dst, wave, lane);
+          }
+        }
+        if (need && lane == 0) *rerun_flag = 1;
         __syncthreads();
-        const int nvalid = min(kPage, L - j * kPage);
-        if (!kFp8 && nvalid < kPage) {            // the sequence's last, partial page
-          zero_tail_rows(cur ? page1 : page0, nvalid, tid);
-          __syncthreads();
-        }
-        if (j + 1 < hi) issue(j + 1, kFp8 ? (cur ? stage0 : stage1) : (cur ? page0 : page1));
-        const LDS_AS uint8_t *pg;
-        if (kFp8) {
-          widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane, nvalid);
-          __syncthreads();
-          pg = page0;
-        } else {
-          pg = cur ? page1 : page0;
-        }
-        if (active)
-          need |= attend_page(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2, (j + 1) * kPage > nvis_min);
-      }
-      if (need && lane == 0) *rerun_flag = 1;
-      __syncthreads();
-      const bool again = (*rerun_flag != 0) && (pass + 1 < kMaxPasses);   // workgroup-uniform
-      __syncthreads();
-      if (!again) break;
-      if (tid == 0) *rerun_flag = 0;
-      if (m_restart != kNegInf) m = m_restart;
-      m_restart = kNegInf;
-      l = 0.f;
+        const bool again = (*rerun_flag != 0) && (pass + 1 < kMaxPasses);   // workgroup-uniform
+        __syncthreads();
+        if (!again) break;
+        if (tid == 0) *rerun_flag = 0;
+        if (m_restart != kNegInf) m = m_restart;
+        m_restart = kNegInf;
+        l = 0.f;
 #pragma unroll
-      for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+        for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+      }
     }
-  }
 
-  // Epilogue: lane holds head `row`, dims 32*t + 8*(i/4) + 4*hl + i%4 of o[t][i].
-  if (active && row_ok) {
-    const bool has = l > 0.f;
-    const float inv = has ? 1.f / l : 0.f;
-    const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
-    if (nsplit <= 1) {
-      uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + 4 * hl;
-      const float f = inv * a.v_scale;
+    // Epilogue: lane holds head `row`, dims 32*t + 8*(i/4) + 4*hl + i%4 of o[t][i].
+    // A sequence with one split writes out / lse; otherwise the split writes
+    // its normalised output (bf16) and lse to its partial slot, which is its
+    // split number num_splits[b] + k.
+    if (active && row_ok) {
+      const bool has = l > 0.f;
+      const float inv = has ? 1.f / l : 0.f;
+      const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
+      const bool direct = nsplit <= 1;
+      const long prow = ((long)slot * a.hk + hk) * a.rows + row;
+      uint16_t *dst = direct ? a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV
+                             : a.part_o + prow * kHeadDimV;
+      dst += 4 * hl;
+      const float f = direct ? inv * a.v_scale : inv;
 #pragma unroll
       for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const __bf16 v0 = (__bf16)(o[t][4 * q4 + 0] * f), v1 = (__bf16)(o[t][4 * q4 + 1] * f);
           const __bf16 v2 = (__bf16)(o[t][4 * q4 + 2] * f), v3 = (__bf16)(o[t][4 * q4 + 3] * f);
-          *(bf16x4 *)(orow + 32 * t + 8 * q4) = bf16x4{v0, v1, v2, v3};
+          *(bf16x4 *)(dst + 32 * t + 8 * q4) = bf16x4{v0, v1, v2, v3};
         }
-      if (hl == 0) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
-    } else {
-      // Partial slot of split k of b is its table row, num_splits[b] + k.
-      const long prow = ((long)seg * a.hk + hk) * a.rows + row;
-      float *po = a.part_o + prow * kHeadDimV + 4 * hl;
-#pragma unroll
-      for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *(f32x4 *)(po + 32 * t + 8 * q4) =
-              f32x4{o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv};
-      if (hl == 0) a.part_lse[prow] = lse_v;
+      if (hl == 0) {
+        if (direct) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
+        else a.part_lse[prow] = lse_v;
+      }
     }
   }
 }
@@ -514,31 +563,26 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
   const float *pl = a.part_lse + ((long)slot0 * a.hk + hk) * a.rows + row;
   float mu = kNegInf;
   for (int k = 0; k < n; ++k) mu = fmaxf(mu, pl[k * sstride]);
-  f32x4 acc0 = {}, acc1 = {};
+  float acc[8] = {};
   float Z = 0.f;
   if (mu != kNegInf) {
-    const float *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
+    const uint16_t *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
     for (int k = 0; k < n; ++k) {
       const float w = __builtin_amdgcn_exp2f((pl[k * sstride] - mu) * kLog2e);
       Z += w;
-      const f32x4 v0 = *(const f32x4 *)(po + k * sstride * kHeadDimV);
-      const f32x4 v1 = *(const f32x4 *)(po + k * sstride * kHeadDimV + 4);
-      acc0 += w * v0;
-      acc1 += w * v1;
+      const bf16x8 v = *(const bf16x8 *)(po + k * sstride * kHeadDimV);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
     }
   }
   const float inv = Z > 0.f ? a.v_scale / Z : 0.f;
   const int qi = row / a.group;
   const int h = hk * a.group + (row - qi * a.group);
   uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + lane * 8;
-  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-  bf16x8_t ov;
+  bf16x8 ov;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ov[e] = (__bf16)(acc0[e] * inv);
-    ov[4 + e] = (__bf16)(acc1[e] * inv);
-  }
-  *(bf16x8_t *)orow = ov;
+  for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(acc[e] * inv);
+  *(bf16x8 *)orow = ov;
   if (lane == 0) a.lse[((long)b * a.hq + h) * a.s_q + qi] = Z > 0.f ? mu + __logf(Z) : kNegInf;
 }
 
@@ -547,7 +591,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const size_t smem = 2 * (size_t)kPageBytes + 16;   // pages (or page + fp8 staging) + restart flag
   static_assert(kPageBytes + 2 * kF8PageBytes == 2 * kPageBytes, "fp8 staging fills the second page slot");
-  const dim3 grid(a.batch + a.num_parts - 1, a.row_tiles * a.hk);
+  const dim3 grid(a.num_parts, a.row_tiles * a.hk);   // one persistent workgroup per part
   if (a.kv_fp8) {
     hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

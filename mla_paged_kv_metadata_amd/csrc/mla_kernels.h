@@ -17,11 +17,11 @@ struct DecodeArgs {
   const uint8_t *kv;          // [num_blocks][64][Hk][576] bf16 or e4m3fn
   const int32_t *block_table; // [B][max_blocks]
   const int32_t *seqlens;     // [B]
-  const int32_t *tile_md;     // [batch + num_parts - 1][8], one row per split
+  const int32_t *tile_md;     // [num_parts][8], one row per part
   const int32_t *num_splits;  // [B+1]
   uint16_t *out;              // bf16 bits [B][s_q][Hq][512]
   float *lse;                 // [B][Hq][s_q]
-  float *part_o;              // [slots][Hk][M][512]
+  uint16_t *part_o;           // bf16 bits [slots][Hk][M][512], slots = batch + num_parts - 1
   float *part_lse;            // [slots][Hk][M]
   int batch, s_q, hq, hk, group, rows, max_blocks, row_tiles, num_parts, num_blocks;
   int kv_fp8, causal;

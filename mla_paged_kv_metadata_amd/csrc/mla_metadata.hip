@@ -8,12 +8,15 @@
 //   units of all sequences are laid end to end in batch order; part p owns
 //   units [p*W, (p+1)*W) with W = ceil(total / num_parts).  Part p works on
 //   sequence b if it owns one of b's page units (or, when b has no pages, b's
-//   first unit); each such pair is one split of b.
-// The table lists every split as its own row (batch + num_parts - 1 rows, the
-// most splits possible): row num_splits[b] + k is split k of sequence b, so a
-// decode workgroup handles exactly one (sequence, page range).  Every entry
-// is a closed form of two prefix sums, so one workgroup computes the table in
-// O(batch + rows) with no device-to-host traffic.
+//   first unit); each such pair is one split of b, numbered k = 0, 1, ... in
+//   part order.
+// Row p of the table tells the persistent decode workgroup of part p what to
+// do: [b0, first page of b0, b1, end page of b1, k of b0's split, W,
+// fixed_cost, splits of the part] -- sequences strictly between b0 and b1 are
+// whole.  Idle parts get b0 = b1 = -1.  Every entry is a closed form of the
+// cost prefix sum (and num_splits of the split-count prefix sum), so one
+// workgroup computes everything in O(batch + parts log batch) with no
+// device-to-host traffic.
 #include "mla_kernels.h"
 
 namespace mla {
@@ -24,29 +27,40 @@ constexpr int kT = kMetaThreads;
 __device__ __forceinline__ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // Exclusive scan over `n` int64 values held in smem[0..n), in place; smem[n] = total.
-// Each thread scans a contiguous chunk; chunk sums are scanned in `tmp`.
+// Each thread scans a contiguous chunk; chunk sums are scanned within each
+// wave by shuffles, then across the kT / 64 wave totals (held in `tmp`).
 __device__ void block_exclusive_scan(long long *smem, int n, long long *tmp) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + kT - 1) / kT;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   long long s = 0;
   for (int i = lo; i < hi; ++i) s += smem[i];
-  tmp[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kT; off <<= 1) {      // Hillis-Steele inclusive scan of chunk sums
-    long long v = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
+  long long incl = s;                              // inclusive scan of chunk sums within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  long long run = tid ? tmp[tid - 1] : 0;
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    long long run = 0;
+    for (int w = 0; w < kT / 64; ++w) {
+      const long long t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[kT / 64] = run;
+  }
+  __syncthreads();
+  long long run = tmp[wave] + incl - s;
   for (int i = lo; i < hi; ++i) {
-    long long x = smem[i];
+    const long long x = smem[i];
     smem[i] = run;
     run += x;
   }
   __syncthreads();
-  if (tid == kT - 1) smem[n] = tmp[kT - 1];
+  if (tid == 0) smem[n] = tmp[kT / 64];
   __syncthreads();
 }
 
@@ -86,31 +100,42 @@ __global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restr
   block_exclusive_scan(cnt, B, tmp);
   for (int b = tid; b <= B; b += kT) num_splits[b] = (int32_t)cnt[b];
 
-  const long long splits = cnt[B];
-  const int rows = B + num_parts - 1;
-  for (int r = tid; r < rows; r += kT) {
-    int32_t *row = tile_md + (size_t)r * 8;
+  // Row p in closed form.  Part p owns units [pW, (p+1)W); it works on
+  // sequence b when it owns one of b's page units [s_b, s_b + nblk_b), or,
+  // for b without pages, b's first unit.  Its first sequence is the one
+  // holding unit pW or the next one; its last is the one holding its last
+  // unit or the one before.
+  auto works = [&](long long p, int b) -> bool {
+    const long long nblk = pref[b + 1] - pref[b] - fc, s = pref[b] + fc;
+    if (nblk > 0) return s + nblk > p * W && s < (p + 1) * W;
+    return pref[b] / W == p;
+  };
+  for (int p = tid; p < num_parts; p += kT) {
+    int32_t *row = tile_md + (size_t)p * 8;
+    const long long u0 = (long long)p * W, u1 = min((long long)(p + 1) * W, total);
+    int b0 = -1, b1 = -1;
+    if (u0 < total) {
+      const int b = upper_index(pref, B, u0);
+      b0 = works(p, b) ? b : (b + 1 < B && works(p, b + 1) ? b + 1 : -1);
+      if (b0 >= 0) {
+        const int e = upper_index(pref, B, u1 - 1);
+        b1 = works(p, e) ? e : e - 1;
+      }
+    }
     row[5] = (int32_t)W;
     row[6] = fixed_cost;
-    if (r >= splits) {
-      row[0] = -1; row[1] = 0; row[2] = 0; row[3] = 0; row[4] = 0; row[7] = -1;
+    if (b0 < 0) {
+      row[0] = -1; row[1] = 0; row[2] = -1; row[3] = 0; row[4] = 0; row[7] = 0;
       continue;
     }
-    const int b = upper_index(cnt, B, r);                   // cnt strictly increasing
-    const long long k = r - cnt[b];
-    const long long n = cnt[b + 1] - cnt[b];
-    const long long nblk = pref[b + 1] - pref[b] - fc;
-    const long long s = pref[b] + fc;
-    long long p, first = 0, end = 0;
-    if (nblk > 0) {
-      p = s / W + k;
-      first = max(0LL, p * W - s);
-      end = min(nblk, (p + 1) * W - s);
-    } else {
-      p = pref[b] / W;
-    }
-    row[0] = b; row[1] = (int32_t)first; row[2] = (int32_t)end; row[3] = (int32_t)k; row[4] = (int32_t)n;
-    row[7] = (int32_t)p;
+    const long long n0 = pref[b0 + 1] - pref[b0] - fc, s0 = pref[b0] + fc;
+    const long long n1 = pref[b1 + 1] - pref[b1] - fc, s1 = pref[b1] + fc;
+    row[0] = b0;
+    row[1] = n0 > 0 ? (int32_t)max(0LL, u0 - s0) : 0;
+    row[2] = b1;
+    row[3] = n1 > 0 ? (int32_t)min(n1, (long long)(p + 1) * W - s1) : 0;
+    row[4] = n0 > 0 ? (int32_t)(p - s0 / W) : 0;
+    row[7] = b1 - b0 + 1;
   }
 }
 

@@ -17,4 +17,4 @@ from .mla_oracle import (  # noqa: F401
     mla_decode_f64,
     visible_keys,
 )
-from .schedule_oracle import check_schedule, schedule  # noqa: F401
+from .schedule_oracle import check_schedule, expand_splits, schedule  # noqa: F401

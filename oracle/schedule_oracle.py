@@ -16,10 +16,13 @@ units so the GPU scheduler kernel can be compared with it bit for bit:
     k = 0, 1, ... in part order.
   * num_splits is the exclusive prefix sum of the split counts:
     num_splits[0] = 0, num_splits[b+1] - num_splits[b] >= 1.
-  * The table has batch + num_parts - 1 rows (the most splits possible).  Row
-    s = num_splits[b] + k describes split k of sequence b as 8 int32:
-    [b, first page, end page (exclusive), k, split count of b, W, fixed_cost,
-    part].  Rows past the last split are [-1, 0, 0, 0, 0, W, fixed_cost, -1].
+  * The table has one row per part (num_parts rows of 8 int32).  A part works
+    on a run of consecutive sequences b0..b1: its first split is split k0 of
+    b0 over pages [first, nblk_b0) (or [first, end) when b0 == b1), the
+    sequences strictly between are whole, and its last split covers pages
+    [0, end) of b1.  Row p = [b0, first, b1, end, k0, W, fixed_cost, number of
+    splits of the part].  A part with no split has [-1, 0, -1, 0, 0, W,
+    fixed_cost, 0].
 """
 from __future__ import annotations
 
@@ -28,12 +31,8 @@ import numpy as np
 TILE_MD_INTS = 8
 
 
-def table_rows(batch: int, num_parts: int) -> int:
-    return batch + num_parts - 1
-
-
 def schedule(cache_seqlens, num_parts: int, fixed_cost: int, page: int = 64):
-    """Returns (tile_md (batch + num_parts - 1, 8) int32, num_splits (B+1,) int32)."""
+    """Returns (tile_md (num_parts, 8) int32, num_splits (B+1,) int32)."""
     L = [int(x) for x in cache_seqlens]
     B = len(L)
     if num_parts < 1 or fixed_cost < 1 or B < 1:
@@ -58,60 +57,87 @@ def schedule(cache_seqlens, num_parts: int, fixed_cost: int, page: int = 64):
     num_splits = np.zeros(B + 1, dtype=np.int32)
     for b in range(B):
         num_splits[b + 1] = num_splits[b] + len(parts_of[b])
-    rows = table_rows(B, num_parts)
-    md = np.zeros((rows, TILE_MD_INTS), dtype=np.int32)
-    md[:] = [-1, 0, 0, 0, 0, W, fixed_cost, -1]
-    for b in range(B):
-        n = len(parts_of[b])
-        for k, p in enumerate(parts_of[b]):
-            pg = pages[p][b]
-            first, end = (pg[0], pg[-1] + 1) if pg else (0, 0)
-            md[num_splits[b] + k] = [b, first, end, k, n, W, fixed_cost, p]
+    md = np.zeros((num_parts, TILE_MD_INTS), dtype=np.int32)
+    md[:] = [-1, 0, -1, 0, 0, W, fixed_cost, 0]
+    for p in range(num_parts):
+        seqs = sorted(pages[p])
+        if not seqs:
+            continue
+        b0, b1 = seqs[0], seqs[-1]
+        pg0, pg1 = pages[p][b0], pages[p][b1]
+        first = pg0[0] if pg0 else 0
+        end = pg1[-1] + 1 if pg1 else 0
+        k0 = parts_of[b0].index(p)
+        md[p] = [b0, first, b1, end, k0, W, fixed_cost, len(seqs)]
     return md, num_splits
+
+
+def expand_splits(tile_md, cache_seqlens, page: int = 64):
+    """Lists the splits a per-part table describes, in table order, as tuples
+    (part, b, k, first page, end page).  Sequences strictly inside a part's
+    run are whole; the run's first and last sequences are cut as the row says."""
+    md = np.asarray(tile_md)
+    L = [int(x) for x in cache_seqlens]
+    out = []
+    for p, r in enumerate(md):
+        b0, first, b1, end, k0 = (int(x) for x in r[:5])
+        if b0 < 0:
+            continue
+        for b in range(b0, b1 + 1):
+            nblk = -(-L[b] // page)
+            lo = first if b == b0 else 0
+            hi = end if b == b1 else nblk
+            out.append((p, b, k0 if b == b0 else 0, lo, hi))
+    return out
 
 
 def check_schedule(tile_md, num_splits, cache_seqlens, num_parts, fixed_cost, page=64):
     """Invariants any valid table must satisfy (raises AssertionError).
 
     Every page of every sequence is covered exactly once and in order by its
-    splits, which occupy consecutive rows starting at num_splits[b] with
-    k = 0, 1, ...; the parts of one sequence's splits are consecutive; every
-    sequence gets >= 1 split; total splits <= B + num_parts - 1; each part's
-    real cost (its pages plus fixed_cost per sequence whose pages it touches)
-    is at most W + fixed_cost; rows past the last split are empty.
+    splits, numbered k = 0, 1, ... in part order; every sequence gets >= 1
+    split and num_splits counts them; total splits <= B + num_parts - 1; the
+    parts of one sequence's splits are consecutive; each part's real cost (its
+    pages plus fixed_cost per sequence whose pages it touches) is at most
+    W + fixed_cost; idle rows are empty; the split count field is right.
     """
     md = np.asarray(tile_md)
     ns = np.asarray(num_splits)
     L = [int(x) for x in cache_seqlens]
     B = len(L)
     nblk = [-(-x // page) for x in L]
-    rows = table_rows(B, num_parts)
-    assert md.shape == (rows, TILE_MD_INTS)
+    assert md.shape == (num_parts, TILE_MD_INTS)
     assert ns.shape == (B + 1,) and ns[0] == 0
     counts = np.diff(ns)
     assert (counts >= 1).all()
-    total = int(ns[-1])
-    assert total <= rows
+    assert int(ns[-1]) <= B + num_parts - 1
     W = int(md[0, 5])
     assert (md[:, 5] == W).all() and (md[:, 6] == fixed_cost).all()
+    for r in md:
+        if r[0] < 0:
+            assert r.tolist() == [-1, 0, -1, 0, 0, W, fixed_cost, 0]
+        else:
+            assert 0 <= r[0] <= r[2] < B and r[7] == r[2] - r[0] + 1
+    splits = expand_splits(md, L, page)
+    seen = {b: [] for b in range(B)}
+    ks = {b: [] for b in range(B)}
+    parts = {b: [] for b in range(B)}
     cost = {}
+    prev_b = -1
+    for p, b, k, lo, hi in splits:
+        assert b >= prev_b                # sequences appear in batch order
+        prev_b = b
+        assert 0 <= lo <= hi <= nblk[b], (p, b, lo, hi)
+        assert hi > lo or nblk[b] == 0, (p, b, lo, hi)
+        seen[b].extend(range(lo, hi))
+        ks[b].append(k)
+        parts[b].append(p)
+        if hi > lo:
+            cost[p] = cost.get(p, 0) + fixed_cost + (hi - lo)
     for b in range(B):
-        seen = []
-        parts = []
-        for k in range(counts[b]):
-            r = md[ns[b] + k]
-            assert r[0] == b and r[3] == k and r[4] == counts[b], (b, k, r)
-            assert 0 <= r[1] <= r[2] <= nblk[b]
-            assert r[2] > r[1] or nblk[b] == 0
-            seen.extend(range(r[1], r[2]))
-            parts.append(int(r[7]))
-            if r[2] > r[1]:
-                cost[int(r[7])] = cost.get(int(r[7]), 0) + fixed_cost + int(r[2] - r[1])
-        assert seen == list(range(nblk[b])), b
-        assert parts == list(range(parts[0], parts[0] + len(parts))), (b, parts)
-        assert all(0 <= p < num_parts for p in parts)
+        assert seen[b] == list(range(nblk[b])), b
+        assert ks[b] == list(range(counts[b])), (b, ks[b], counts[b])
+        assert parts[b] == list(range(parts[b][0], parts[b][0] + len(parts[b]))), (b, parts[b])
     for p, c in cost.items():
         assert c <= W + fixed_cost, (p, c, W)
-    for r in md[total:]:
-        assert r[0] == -1 and r[7] == -1
     return True

@@ -42,7 +42,7 @@ def test_status_strings():
 def test_workspace_bytes():
     n = mla.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
     slots = 64 + 256
-    assert n >= slots * 128 * 512 * 4 + slots * 128 * 4
+    assert n >= slots * 128 * 512 * 2 + slots * 128 * 4      # bf16 partial outputs, fp32 lse
     with pytest.raises(mla.MlaError) as e:
         mla.mla_workspace_bytes(0, 1, 128, 1, 512, 256)
     assert e.value.status == 1
@@ -63,7 +63,7 @@ def _decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), 1), (dict(out=0), 1), (dict(lse=0), 1), (dict(batch=0), 1), (dict(hq=6, hk=4), 1),
-    (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(d=192), 2), (dict(dv=128), 2),
+    (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(scale=-0.5), 2), (dict(d=192), 2), (dict(dv=128), 2),
     (dict(page=16), 2), (dict(dt=7), 2), (dict(s_q=9, hq=128), 2), (dict(batch=9000), 2),
     (dict(wsb=16), 3), (dict(ws=0), 3),
 ])

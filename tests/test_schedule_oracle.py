@@ -9,7 +9,7 @@ itself pinned by planting mistakes in valid tables.
 import numpy as np
 import pytest
 
-from oracle import check_schedule, schedule
+from oracle import check_schedule, expand_splits, schedule
 from workloads import make_config
 
 
@@ -48,9 +48,22 @@ def test_single_part_takes_everything_in_one_split_each():
     L = [5, 700, 0, 64]
     md, ns = schedule(L, 1, 2)
     assert ns.tolist() == [0, 1, 2, 3, 4]
-    assert md.shape == (4, 8)
-    assert md[:, :5].tolist() == [[0, 0, 1, 0, 1], [1, 0, 11, 0, 1], [2, 0, 0, 0, 1], [3, 0, 1, 0, 1]]
-    assert (md[:, 7] == 0).all()
+    assert md.tolist() == [[0, 0, 3, 1, 0, 2 * 4 + 1 + 11 + 0 + 1, 2, 4]]
+    assert expand_splits(md, L) == [(0, 0, 0, 0, 1), (0, 1, 0, 0, 11), (0, 2, 0, 0, 0), (0, 3, 0, 0, 1)]
+
+
+def test_hand_worked_two_part_table():
+    # Units (fixed_cost 1): b0 = [o, p0, p1], b1 = [o, p0, p1, p2, p3]; total 8,
+    # W = 4: part 0 owns b0 whole and b1's overhead unit (no page of b1), part 1
+    # owns b1's pages 0..3.
+    md, ns = schedule([128, 256], 2, 1)
+    assert ns.tolist() == [0, 1, 2]
+    assert md.tolist() == [[0, 0, 0, 2, 0, 4, 1, 1], [1, 0, 1, 4, 0, 4, 1, 1]]
+    # W = 3 with three parts: part 0 = b0 whole; part 1 = b1's overhead + pages
+    # 0, 1; part 2 = b1's pages 2, 3.
+    md, ns = schedule([128, 256], 3, 1)
+    assert ns.tolist() == [0, 1, 3]
+    assert md.tolist() == [[0, 0, 0, 2, 0, 3, 1, 1], [1, 0, 1, 2, 0, 3, 1, 1], [1, 2, 1, 4, 1, 3, 1, 1]]
 
 
 def test_long_sequence_is_spread_over_many_parts():
@@ -60,27 +73,28 @@ def test_long_sequence_is_spread_over_many_parts():
 
 
 @pytest.mark.parametrize("mutation", ["drop_page", "dup_page", "bad_rank", "bad_count", "overload", "part_gap",
-                                      "stray_row"])
+                                      "stray_row", "bad_nsplit"])
 def test_checker_catches_planted_mistakes(mutation):
     L = [300, 129, 64, 1000]
     md, ns = schedule(L, 6, 2)
     md = md.copy()
     ns = ns.copy()
+    cut = next(p for p in range(len(md)) if md[p, 4] > 0)      # a part starting mid-sequence
     if mutation == "drop_page":
-        md[0, 2] -= 1
+        md[cut, 1] += 1
     elif mutation == "dup_page":
-        md[1, 1] -= 1
+        md[cut, 1] -= 1
     elif mutation == "bad_rank":
-        k = next(s for s in range(len(md)) if md[s, 3] > 0)
-        md[k, 3] += 1
+        md[cut, 4] += 1
     elif mutation == "bad_count":
         ns[2:] += 1
     elif mutation == "overload":
         md[:, 5] = 1                      # claimed payload too small for the real costs
     elif mutation == "part_gap":
-        k = next(s for s in range(len(md)) if md[s, 3] > 0)
-        md[k, 7] += 1
+        md[cut - 1:cut + 1] = md[[cut, cut - 1]]    # two parts swapped
     elif mutation == "stray_row":
-        md[-1, 0] = 2
+        md[-1] = [2, 0, 2, 1, 0, md[0, 5], 2, 1]
+    elif mutation == "bad_nsplit":
+        md[cut, 7] += 1
     with pytest.raises(AssertionError):
         check_schedule(md, ns, L, 6, 2)
