@@ -168,6 +168,10 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   const long rows = (long)s_q * group;
   if (rows > MLA_MAX_ROWS) return fail(MLA_ERR_UNSUPPORTED, "s_q * num_heads_q / num_heads_k exceeds MLA_MAX_ROWS");
   if (batch > MLA_MAX_BATCH) return fail(MLA_ERR_UNSUPPORTED, "batch exceeds MLA_MAX_BATCH");
+  // Row indices of out and of the partial slots are 32-bit in the kernels.
+  if ((long long)batch * s_q * num_heads_q >= (1LL << 31) ||
+      ((long long)batch + num_parts) * rows * num_heads_k >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * num_heads_q or the partial slots exceed 2^31 rows");
   size_t need = 0;
   int rc = mla_workspace_bytes(batch, s_q, num_heads_q, num_heads_k, head_dim_v, num_parts, &need);
   if (rc) return rc;

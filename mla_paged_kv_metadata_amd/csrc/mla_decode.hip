@@ -42,6 +42,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -85,36 +86,54 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane i's
-// 16 bytes land at lds + 16 * i.  Written as inline assembly on purpose: the
-// compiler cannot tell which LDS bytes a copy writes, so for its own copy
-// intrinsic it waits for every copy in flight before any later transposing
-// LDS read -- which would serialise the next page's copy with this page's PV
-// product.  Completion is instead awaited explicitly (wait_vmcnt) before the
-// barrier that publishes a page.  M0 holds the LDS base; an M0 write needs
-// one wait state before an LDS-DMA instruction.
-__device__ __forceinline__ void lds_dma16(const void *src, LDS_AS void *lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "m0");
+// 16 bytes from src + kImm land at lds + 16 * i.  Written as inline assembly
+// on purpose: the compiler cannot tell which LDS bytes a copy writes, so for
+// its own copy intrinsic it waits for every copy in flight before any later
+// transposing LDS read -- which would serialise the next page's copy with
+// this page's PV product.  Completion is instead awaited explicitly
+// (wait_vmcnt) before the barrier that publishes a page.  M0 holds the LDS
+// base; an M0 write needs one wait state before an LDS-DMA instruction.  The
+// instruction's immediate offset applies to the global and the LDS address
+// alike, so M0 is lowered by it.
+template <int kImm>
+__device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) {
+  static_assert(kImm >= 0 && kImm < 4096, "global offset field");
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds) - kImm;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "s"(base),
+               "n"(kImm)
+               : "m0");
 }
 
 // HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above,
-// as kPageLoads wave instructions per wave.  Wave instruction I covers group
-// I/8, tokens 8*(I%8) .. +7.  The whole page is copied; rows past the
-// sequence end are zeroed in LDS afterwards (zero_tail_rows) before any wave
-// reads them.  dma_bf16_step issues instruction k of this wave.
-__device__ __forceinline__ void dma_bf16_step(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
-                                              int lane, int k) {
+// as kPageLoads wave instructions per wave.  The LDS image is 72 slots of
+// 1 KiB, slot I = 8 * group + token block (8 tokens); wave w copies token
+// blocks 2w and 2w + 1 of every group, instruction k covering block
+// 2w + (k & 1) of group k / 2.  Per lane the source is one of two lane
+// addresses (k even / odd) plus the immediate 128 * (k / 2).  The whole page
+// is copied; rows past the sequence end are zeroed in LDS afterwards
+// (zero_tail_rows) before any wave reads them.
+struct PageSrc {
+  const uint8_t *even, *odd;   // this lane's source for token blocks 2w, 2w + 1 (group 0)
+};
+__device__ __forceinline__ PageSrc page_src_bf16(const uint8_t *tok0, int tok_stride, int wave, int lane) {
   const int lt = lane >> 3;
-  const int I = wave * kPageLoads + k;
-  // token 8*(I%8) + lt: h(token) = (lt1, lt2, (I%8)&1) -> the low bit varies with I
-  const int lane_off = lt * tok_stride + ((lane & 7) ^ swz_h(lt + 8 * (I & 1))) * 16;
-  const uint8_t *src = tok0 + ((I & 7) * 8 * tok_stride + (I >> 3) * 128);
-  lds_dma16(src + lane_off, dst + I * 1024);
+  // token t = 16w + 8*(k&1) + lt: h(t) = (lt1, lt2, k&1) -> chunk (lane & 7) ^ h(t)
+  PageSrc p;
+  p.even = tok0 + (16 * wave + lt) * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;
+  p.odd = tok0 + (16 * wave + 8 + lt) * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
+  return p;
 }
-__device__ __forceinline__ void dma_page_bf16(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
-                                              int lane) {
-#pragma unroll
-  for (int k = 0; k < kPageLoads; ++k) dma_bf16_step(tok0, tok_stride, dst, wave, lane, k);
+template <int k>
+__device__ __forceinline__ void dma_bf16_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
+  const int I = 8 * (k >> 1) + 2 * wave + (k & 1);
+  lds_dma16<128 * (k >> 1)>((k & 1) ? p.odd : p.even, dst + I * 1024);
+}
+template <int k = 0>
+__device__ __forceinline__ void dma_page_bf16(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
+  if constexpr (k < kPageLoads) {
+    dma_bf16_step<k>(p, dst, wave);
+    dma_page_bf16<k + 1>(p, dst, wave);
+  }
 }
 
 // Zero rows nvalid..63 of a bf16 page in LDS (the cache rows past a
@@ -127,19 +146,48 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid,
   }
 }
 
-// HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: wave
-// instruction I covers chunks 4*(I/4) .. +3 of tokens 16*(I%4) .. +15.
-__device__ __forceinline__ void dma_fp8_step(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
-                                             int lane, int k) {
-  const int lane_off = (lane >> 2) * tok_stride + (lane & 3) * 16;
-  const int I = wave * kF8PageLoads + k;
-  const uint8_t *src = tok0 + ((I & 3) * 16 * tok_stride + (I >> 2) * 64);
-  lds_dma16(src + lane_off, dst + I * 1024);
+// HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: slot
+// I = 4 * (column group of 64 B) + token block (16 tokens); wave w copies
+// token block w, instruction k covering column group k.
+__device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *tok0, int tok_stride, int wave, int lane) {
+  PageSrc p;
+  p.even = p.odd = tok0 + (16 * wave + (lane >> 2)) * tok_stride + (lane & 3) * 16;
+  return p;
 }
-__device__ __forceinline__ void dma_page_fp8(const uint8_t *tok0, int tok_stride, LDS_AS uint8_t *dst, int wave,
-                                             int lane) {
-#pragma unroll
-  for (int k = 0; k < kF8PageLoads; ++k) dma_fp8_step(tok0, tok_stride, dst, wave, lane, k);
+template <int k>
+__device__ __forceinline__ void dma_fp8_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
+  lds_dma16<64 * k>(p.even, dst + (4 * k + wave) * 1024);
+}
+template <int k = 0>
+__device__ __forceinline__ void dma_page_fp8(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
+  if constexpr (k < kF8PageLoads) {
+    dma_fp8_step<k>(p, dst, wave);
+    dma_page_fp8<k + 1>(p, dst, wave);
+  }
+}
+
+// Instruction k of a page copy for a k known only after loop unrolling (the
+// switch folds away once k is a constant).
+__device__ __forceinline__ void dma_bf16_dispatch(const PageSrc &p, LDS_AS uint8_t *dst, int wave, int k) {
+  switch (k) {
+#define MLA_DMA_CASE(n) \
+  case n: dma_bf16_step<n>(p, dst, wave); break;
+    MLA_DMA_CASE(0) MLA_DMA_CASE(1) MLA_DMA_CASE(2) MLA_DMA_CASE(3) MLA_DMA_CASE(4) MLA_DMA_CASE(5)
+    MLA_DMA_CASE(6) MLA_DMA_CASE(7) MLA_DMA_CASE(8) MLA_DMA_CASE(9) MLA_DMA_CASE(10) MLA_DMA_CASE(11)
+    MLA_DMA_CASE(12) MLA_DMA_CASE(13) MLA_DMA_CASE(14) MLA_DMA_CASE(15) MLA_DMA_CASE(16) MLA_DMA_CASE(17)
+#undef MLA_DMA_CASE
+    default: break;
+  }
+}
+__device__ __forceinline__ void dma_fp8_dispatch(const PageSrc &p, LDS_AS uint8_t *dst, int wave, int k) {
+  switch (k) {
+#define MLA_DMA_CASE(n) \
+  case n: dma_fp8_step<n>(p, dst, wave); break;
+    MLA_DMA_CASE(0) MLA_DMA_CASE(1) MLA_DMA_CASE(2) MLA_DMA_CASE(3) MLA_DMA_CASE(4) MLA_DMA_CASE(5)
+    MLA_DMA_CASE(6) MLA_DMA_CASE(7) MLA_DMA_CASE(8)
+#undef MLA_DMA_CASE
+    default: break;
+  }
 }
 
 // Two floats that hold bf16-exact values -> packed bf16 pair (truncation is exact here).
@@ -228,9 +276,8 @@ __device__ __forceinline__ float sum_across_halves(float v) {
 // issued in one burst, so the wave keeps feeding the matrix core while the
 // address unit drains them.
 struct NextPage {
-  const uint8_t *tok0;        // cache row of the next page's first token (this KV head)
+  PageSrc src;                // this lane's source addresses of the next page
   LDS_AS uint8_t *dst;        // its LDS (bf16 page or fp8 staging) buffer
-  int tok_stride;
   int wave;
   bool valid;                 // workgroup-uniform
 };
@@ -307,9 +354,11 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
       k0[sl] = kload(ks + kPre, 0);
       k1[sl] = kload(ks + kPre, 1);
     }
-    if (nx.valid && ks < (kFp8 ? kF8PageLoads : kPageLoads)) {
-      if (kFp8) dma_fp8_step(nx.tok0, nx.tok_stride, nx.dst, nx.wave, lane, ks);
-      else dma_bf16_step(nx.tok0, nx.tok_stride, nx.dst, nx.wave, lane, ks);
+    // One copy instruction every other k-step (denser issue stalls the
+    // matrix core more than it gains).
+    if (nx.valid && (ks & 1) == 0 && ks / 2 < (kFp8 ? kF8PageLoads : kPageLoads)) {
+      if (kFp8) dma_fp8_dispatch(nx.src, nx.dst, nx.wave, ks / 2);
+      else dma_bf16_dispatch(nx.src, nx.dst, nx.wave, ks / 2);
     }
     __builtin_amdgcn_sched_barrier(0);                 // keep loads kPre k-steps ahead
   }
@@ -376,15 +425,74 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
 // accumulated as is (still finite up to 2^64 relative weights).
 constexpr int kMaxPasses = 4;
 
+// Rounds a pair of floats to a packed bf16 pair (round to nearest even).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  const bf16x2 v = bf16x2{(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// Writes this wave's 32 x 512 result rows (times f, rounded to bf16) to
+// global memory, coalesced: the O^T accumulators hold one row per lane and
+// 4-dim pieces, so the tile is transposed through LDS (`stage`, 32 rows of
+// 528 bytes per wave, private to the wave) in two rounds of 256 dims.  Per
+// round, pairs of 4-dim pieces are merged into 16-byte chunks across
+// lane ^ 32 with v_permlane32_swap; the 16-byte row padding makes both the
+// column writes (16 rows, one chunk) and the row reads (one row, 16 chunks)
+// conflict-free.  Each read-back instruction covers two whole 512-byte half
+// rows, which go out as one contiguous 16-byte store per lane.
+//   row_idx : this lane's destination row index in units of 512 elements
+//             (lanes 0..31 hold rows 0..31 of the wave)
+//   nrows   : number of valid rows of the wave (0..32)
+constexpr int kStageRow = 528;
+static_assert(4 * 32 * kStageRow <= kPageBytes, "the four waves' staging fits in one page buffer");
+__device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
+                                           int nrows, LDS_AS uint8_t *stage, int lane) {
+  const int r = lane & 31, hl = lane >> 5, c = lane & 31;
+  LDS_AS uint8_t *wr = stage + r * kStageRow + (hl ? 0 : 16);    // lanes < 32 write the odd chunk of a pair
+  const LDS_AS uint8_t *rd = stage + hl * kStageRow + c * 16;    // row 2k + hl, chunk c
+#pragma unroll
+  for (int R = 0; R < 2; ++R) {
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int t = 8 * R + tt;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        // piece q holds dims 8q + 4*hl .. +3 of tile t
+        const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);   // q = 2pp
+        const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
+        const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);   // q = 2pp + 1
+        const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
+        // After the swap lanes < 32 hold chunk q = 2pp + 1, lanes >= 32 chunk 2pp.
+        const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+        *(LDS_AS u32x4 *)(wr + (4 * tt + 2 * pp) * 16) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const u32x4 v = *(const LDS_AS u32x4 *)(rd + 2 * k * kStageRow);
+      const int ra = __builtin_amdgcn_readlane(row_idx, 2 * k), rb = __builtin_amdgcn_readlane(row_idx, 2 * k + 1);
+      if (2 * k + hl < nrows) *(u32x4 *)(base + (long)(hl ? rb : ra) * kHeadDimV + R * 256 + c * 8) = v;
+    }
+  }
+}
+
+// Bijection of [0, n): workgroup w runs on XCD w % 8 (the dispatcher's
+// round-robin); XCD x gets the x-th contiguous block of parts.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_part(int w, int n) {
+  const int q = n / kXcds, r = n % kXcds, x = w % kXcds, i = w / kXcds;
+  return x * q + min(x, r) + i;
+}
+
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
   // bf16: two page buffers.  fp8: one bf16 page + two fp8 staging buffers.
-  LDS_AS uint8_t *page0 = smem;
-  LDS_AS uint8_t *page1 = smem + kPageBytes;
-  LDS_AS uint8_t *stage0 = smem + kPageBytes;
-  LDS_AS uint8_t *stage1 = smem + kPageBytes + kF8PageBytes;
+  LDS_AS uint8_t *const bufs[2] = {smem, smem + kPageBytes};
+  LDS_AS uint8_t *const stages[2] = {smem + kPageBytes, smem + kPageBytes + kF8PageBytes};
+  LDS_AS uint8_t *const page0 = smem;
   volatile LDS_AS int *rerun_flag = (volatile LDS_AS int *)(smem + 2 * kPageBytes);
 
   const int tid = threadIdx.x;
@@ -392,8 +500,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int rt = blockIdx.y % a.row_tiles;
   const int hk = blockIdx.y / a.row_tiles;
   // Table row of this part: a run of sequences b0..b1, the first and last
-  // possibly cut at a page boundary.
-  const int32_t *md = a.tile_md + (long)blockIdx.x * 8;
+  // possibly cut at a page boundary.  Workgroups are dealt to the 8 XCDs
+  // round-robin; consecutive parts (which share sequences, hence q rows and
+  // partial slots) are given to workgroups on the same XCD so that they meet
+  // in its L2.
+  const int part = xcd_part(blockIdx.x, a.num_parts);
+  const int32_t *md = a.tile_md + (long)part * 8;
   const int b0 = md[0];
   if (b0 < 0 || b0 >= a.batch) return;                // idle part
   const int b1 = min(max(md[2], b0), a.batch - 1);
@@ -401,13 +513,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
   const int wrow0 = rt * kRowsPerTile + wave * 32;
   const bool active = wrow0 < a.rows;                 // wave-uniform
+  const int wave_rows = max(0, min(32, a.rows - wrow0));
   const int row = wrow0 + (lane & 31);
-  const bool row_ok = row < a.rows;
-  const int qi = row / a.group;                       // query token of this row
-  const int h = hk * a.group + (row - qi * a.group);  // query head of this row
-  const int rowc = min(row, a.rows - 1);
-  const int qic = rowc / a.group;
-  const int hc = hk * a.group + (rowc - qic * a.group);
+  const int rowc = min(row, a.rows - 1);              // rows past `rows` compute a valid row, never stored
+  const int qi = rowc / a.group;                      // query token of this row
+  const int h = hk * a.group + (rowc - qi * a.group); // query head of this row
   const int hl = lane >> 5;
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
@@ -416,13 +526,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int tok_stride = a.hk * kHeadDim * elem;
   const long page_stride = (long)kPage * tok_stride;
   const uint8_t *kv_head = a.kv + (long)hk * kHeadDim * elem;
+  auto page_addr = [&](int pg) -> const uint8_t * {
+    return kv_head + (long)max(0, min(pg, a.num_blocks - 1)) * page_stride;
+  };
+  // Lengths and page ranges are clamped so that every global address stays
+  // inside its buffer whatever the table or cache_seqlens hold.
+  auto seq_len = [&](int b) { return max(0, min(a.seqlens[b], a.max_blocks * kPage)); };
+  auto seq_end = [&](int b, int nblk) { return b == b1 ? max(0, min(md[3], nblk)) : nblk; };
 
+  bf16x8 qf[kKSteps];
+  // This lane's q fragments: row (qi, h) of sequence b, dims 16 ks + 8 hl .. +7.
+  auto q_row = [&](int b) -> const uint16_t * {
+    return a.q + (((long)min(b, a.batch - 1) * a.s_q + qi) * a.hq + h) * kHeadDim + 8 * hl;
+  };
+  auto load_q = [&](int b) {
+    const uint16_t *qrow = q_row(b);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+  };
+
+  int cur = 0;              // buffer that receives / holds the next page to process
+  bool have_first = false;  // the first page of the current split is already in flight into it
+  {
+    // The part's first page goes out before its q, so both are in flight together.
+    const int nblk0 = (seq_len(b0) + kPage - 1) / kPage;
+    const int hi0 = seq_end(b0, nblk0), lo0 = max(0, min(md[1], hi0));
+    if (hi0 > lo0) {
+      const uint8_t *src = page_addr(a.block_table[(long)b0 * a.max_blocks + lo0]);
+      if (kFp8) dma_page_fp8(page_src_fp8(src, tok_stride, wave, lane), stages[0], wave);
+      else dma_page_bf16(page_src_bf16(src, tok_stride, wave, lane), bufs[0], wave);
+      have_first = true;
+    }
+  }
+  load_q(b0);
   for (int b = b0; b <= b1; ++b) {
-    // Lengths, page ranges and slots are clamped so that every global address
-    // below stays inside its buffer whatever the table or cache_seqlens hold.
-    const int L = max(0, min(a.seqlens[b], a.max_blocks * kPage));
+    const int L = seq_len(b);
     const int nblk = (L + kPage - 1) / kPage;
-    const int hi = b == b1 ? max(0, min(md[3], nblk)) : nblk;
+    const int hi = seq_end(b, nblk);
     const int lo = b == b0 ? max(0, min(md[1], hi)) : 0;
     const int first_slot = a.num_splits[b];
     const int nsplit = a.num_splits[b + 1] - first_slot;
@@ -432,6 +572,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     // the fewest keys): pages at or past it need per-key masking.
     const int nvis_min = a.causal ? max(0, min(L, L - a.s_q + 1 + qi_min)) : L;
     const int32_t *bt = a.block_table + (long)b * a.max_blocks;
+    // First page of the next split of this part (page 0 of b + 1), copied
+    // while the last page of this split is processed.
+    const uint8_t *next_src = kv_head;
+    bool next_has_pages = false;
+    if (b < b1) {
+      const int Ln = seq_len(b + 1);
+      next_has_pages = seq_end(b + 1, (Ln + kPage - 1) / kPage) > 0;
+      if (next_has_pages) next_src = page_addr(a.block_table[(long)(b + 1) * a.max_blocks]);
+    }
     if (tid == 0) *rerun_flag = 0;
 
     float m = kNegInf, l = 0.f, m_restart = kNegInf;
@@ -442,12 +591,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
 
     if (hi > lo) {
-      bf16x8 qf[kKSteps];
-      // Rows past `rows` load a valid row instead (their results are never written).
-      const uint16_t *qrow = a.q + (((long)b * a.s_q + qic) * a.hq + hc) * kHeadDim + 8 * hl;
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
-
       // Block-table entries of the split live in one VGPR, lane i holding the
       // page index of j = bt_base + i, so a page lookup is a v_readlane instead
       // of a global-memory round trip per page; refilled every 64 pages.
@@ -460,52 +603,55 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         }
         return __builtin_amdgcn_readlane(bt_vec, j - bt_base);
       };
-      auto page_src = [&](int j) -> const uint8_t * {
-        const int pgi = max(0, min(page_of(j), a.num_blocks - 1));
-        return kv_head + (long)pgi * page_stride;
-      };
       for (int pass = 0;; ++pass) {
         bool need = false;
-        if (kFp8) dma_page_fp8(page_src(lo), tok_stride, stage0, wave, lane);
-        else dma_page_bf16(page_src(lo), tok_stride, page0, wave, lane);
+        if (!have_first) {
+          if (kFp8) dma_page_fp8(page_src_fp8(page_addr(page_of(lo)), tok_stride, wave, lane), stages[cur], wave);
+          else dma_page_bf16(page_src_bf16(page_addr(page_of(lo)), tok_stride, wave, lane), bufs[cur], wave);
+        }
+        have_first = false;
         for (int j = lo; j < hi; ++j) {
-          const int cur = (j - lo) & 1;
           // Page j has landed in every wave's share; every wave is done with
-          // page j - 1, whose buffer the copy of page j + 1 reuses.
+          // the other buffer, which the copy of the next page reuses.
           wait_vmcnt<0>();
           __syncthreads();
           const int nvalid = min(kPage, L - j * kPage);
           if (!kFp8 && nvalid < kPage) {            // the sequence's last, partial page
-            zero_tail_rows(cur ? page1 : page0, nvalid, tid);
+            zero_tail_rows(bufs[cur], nvalid, tid);
             __syncthreads();
           }
           NextPage nx;
-          nx.valid = j + 1 < hi;
-          nx.tok0 = nx.valid ? page_src(j + 1) : kv_head;
-          nx.dst = kFp8 ? (cur ? stage0 : stage1) : (cur ? page0 : page1);
-          nx.tok_stride = tok_stride;
+          nx.valid = j + 1 < hi || next_has_pages;
+          const uint8_t *ntok0 = j + 1 < hi ? page_addr(page_of(j + 1)) : next_src;
+          nx.src = kFp8 ? page_src_fp8(ntok0, tok_stride, wave, lane) : page_src_bf16(ntok0, tok_stride, wave, lane);
+          nx.dst = kFp8 ? stages[cur ^ 1] : bufs[cur ^ 1];
           nx.wave = wave;
           const LDS_AS uint8_t *pg;
           if (kFp8) {
-            widen_fp8_page(cur ? stage1 : stage0, page0, wave, lane, nvalid);
+            widen_fp8_page(stages[cur], page0, wave, lane, nvalid);
             __syncthreads();
             pg = page0;
           } else {
-            pg = cur ? page1 : page0;
+            pg = bufs[cur];
           }
           if (active) {
             need |= attend_page<kFp8>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
                                       (j + 1) * kPage > nvis_min, nx);
           } else if (nx.valid) {                    // a wave without rows still copies its share
-            if (kFp8) dma_page_fp8(nx.tok0, tok_stride, nx.dst, wave, lane);
-            else dma_page_bf16(nx.tok0, tok_stride, nx.dst, wave, lane);
+            if (kFp8) dma_page_fp8(nx.src, nx.dst, wave);
+            else dma_page_bf16(nx.src, nx.dst, wave);
           }
+          cur ^= 1;
         }
         if (need && lane == 0) *rerun_flag = 1;
         __syncthreads();
         const bool again = (*rerun_flag != 0) && (pass + 1 < kMaxPasses);   // workgroup-uniform
         __syncthreads();
-        if (!again) break;
+        if (!again) {
+          have_first = next_has_pages;              // page 0 of b + 1 is in flight into bufs[cur]
+          break;
+        }
+        wait_vmcnt<0>();                            // drop the copy of the next split's first page
         if (tid == 0) *rerun_flag = 0;
         if (m_restart != kNegInf) m = m_restart;
         m_restart = kNegInf;
@@ -514,40 +660,40 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
       }
     }
-
-    // Epilogue: lane holds head `row`, dims 32*t + 8*(i/4) + 4*hl + i%4 of o[t][i].
-    // A sequence with one split writes out / lse; otherwise the split writes
-    // its normalised output (bf16) and lse to its partial slot, which is its
-    // split number num_splits[b] + k.
-    if (active && row_ok) {
+    // Epilogue.  A sequence with one split writes out / lse; otherwise the
+    // split writes its normalised output (bf16) and lse to its partial slot,
+    // which is its split number num_splits[b] + k.  The results are staged
+    // through the buffer of the split's last page (free once every wave is
+    // past the barriers above; fp8: the bf16 page), never through bufs[cur],
+    // which may be receiving the next split's first page.
+    if (active) {
       const bool has = l > 0.f;
       const float inv = has ? 1.f / l : 0.f;
       const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
       const bool direct = nsplit <= 1;
-      const long prow = ((long)slot * a.hk + hk) * a.rows + row;
-      uint16_t *dst = direct ? a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV
-                             : a.part_o + prow * kHeadDimV;
-      dst += 4 * hl;
-      const float f = direct ? inv * a.v_scale : inv;
-#pragma unroll
-      for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const __bf16 v0 = (__bf16)(o[t][4 * q4 + 0] * f), v1 = (__bf16)(o[t][4 * q4 + 1] * f);
-          const __bf16 v2 = (__bf16)(o[t][4 * q4 + 2] * f), v3 = (__bf16)(o[t][4 * q4 + 3] * f);
-          *(bf16x4 *)(dst + 32 * t + 8 * q4) = bf16x4{v0, v1, v2, v3};
-        }
-      if (hl == 0) {
+      const int prow = (slot * a.hk + hk) * a.rows + rowc;
+      const int orow = ((b * a.s_q + qi) * a.hq + h);
+      LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * (32 * kStageRow);
+      store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow, wave_rows,
+                 stage, lane);
+      if (hl == 0 && row < a.rows) {
         if (direct) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
         else a.part_lse[prow] = lse_v;
       }
     }
+    // The next split's q goes out after the stores (the next page's wait
+    // covers both).
+    if (b < b1) load_q(b + 1);
   }
 }
 
 // Merge the split partials of every sequence with more than one split:
 // out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
-// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.
+// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  One wave per
+// row, 8 dims per lane; the splits are read 8 at a time (all loads of a batch
+// in flight together) with the running max rescaling the sums between
+// batches.
+constexpr int kCombineBatch = 8;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
   const int b = blockIdx.x;
   const int nrows = a.batch + a.num_parts - 1;        // partial slots written by the decode kernel
@@ -561,18 +707,34 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const long sstride = (long)a.hk * a.rows;
   const float *pl = a.part_lse + ((long)slot0 * a.hk + hk) * a.rows + row;
-  float mu = kNegInf;
-  for (int k = 0; k < n; ++k) mu = fmaxf(mu, pl[k * sstride]);
+  const uint16_t *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
+  float mu = kNegInf, Z = 0.f;
   float acc[8] = {};
-  float Z = 0.f;
-  if (mu != kNegInf) {
-    const uint16_t *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
-    for (int k = 0; k < n; ++k) {
-      const float w = __builtin_amdgcn_exp2f((pl[k * sstride] - mu) * kLog2e);
-      Z += w;
-      const bf16x8 v = *(const bf16x8 *)(po + k * sstride * kHeadDimV);
+  for (int k0 = 0; k0 < n; k0 += kCombineBatch) {
+    float lk[kCombineBatch];
+    bf16x8 vk[kCombineBatch];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int k = min(k0 + i, n - 1);               // past n: a repeat, weighted 0 below
+      lk[i] = pl[k * sstride];
+      vk[i] = *(const bf16x8 *)(po + k * sstride * kHeadDimV);
+    }
+    float mb = mu;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i)
+      if (k0 + i < n) mb = fmaxf(mb, lk[i]);
+    if (mb == kNegInf) continue;                      // every split so far is empty
+    const float sc = __builtin_amdgcn_exp2f((mu - mb) * kLog2e);   // 0 while mu = -inf
+    Z *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    mu = mb;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const float w = k0 + i < n ? __builtin_amdgcn_exp2f((lk[i] - mu) * kLog2e) : 0.f;
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * (float)vk[i][e];
     }
   }
   const float inv = Z > 0.f ? a.v_scale / Z : 0.f;
