@@ -445,8 +445,19 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 //   nrows   : number of valid rows of the wave (0..32)
 constexpr int kStageRow = 528;
 static_assert(4 * 32 * kStageRow <= kPageBytes, "the four waves' staging fits in one page buffer");
+// The lane index is re-derived here through an opaque instruction: the
+// lane-dependent addresses below are then computed where they are used
+// instead of being hoisted out of the sequence loop, where they would only
+// be spilled and reloaded (and a reload's wait would stall on the next
+// page's copy and on the stores in flight).
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
-                                           int nrows, LDS_AS uint8_t *stage, int lane) {
+                                           int nrows, LDS_AS uint8_t *stage) {
+  const int lane = lane_id_here();
   const int r = lane & 31, hl = lane >> 5, c = lane & 31;
   LDS_AS uint8_t *wr = stage + r * kStageRow + (hl ? 0 : 16);    // lanes < 32 write the odd chunk of a pair
   const LDS_AS uint8_t *rd = stage + hl * kStageRow + c * 16;    // row 2k + hl, chunk c
@@ -468,11 +479,21 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, 
         *(LDS_AS u32x4 *)(wr + (4 * tt + 2 * pp) * 16) = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
     }
+    // Read-backs in batches of 8 (their latencies overlap), then the stores.
+    // Row validity is tested per row pair with wave-uniform branches.
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x4 v = *(const LDS_AS u32x4 *)(rd + 2 * k * kStageRow);
-      const int ra = __builtin_amdgcn_readlane(row_idx, 2 * k), rb = __builtin_amdgcn_readlane(row_idx, 2 * k + 1);
-      if (2 * k + hl < nrows) *(u32x4 *)(base + (long)(hl ? rb : ra) * kHeadDimV + R * 256 + c * 8) = v;
+    for (int k0 = 0; k0 < 16; k0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *(const LDS_AS u32x4 *)(rd + 2 * (k0 + k) * kStageRow);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int rr = 2 * (k0 + k);
+        const int ra = __builtin_amdgcn_readlane(row_idx, rr), rb = __builtin_amdgcn_readlane(row_idx, rr + 1);
+        uint16_t *dst = base + (long)(hl ? rb : ra) * kHeadDimV + R * 256 + c * 8;
+        if (rr + 1 < nrows) *(u32x4 *)dst = v[k];
+        else if (rr < nrows && hl == 0) *(u32x4 *)dst = v[k];
+      }
     }
   }
 }
@@ -675,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const int orow = ((b * a.s_q + qi) * a.hq + h);
       LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * (32 * kStageRow);
       store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow, wave_rows,
-                 stage, lane);
+                 stage);
       if (hl == 0 && row < a.rows) {
         if (direct) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
         else a.part_lse[prow] = lse_v;
