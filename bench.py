@@ -47,6 +47,124 @@ def work_counts(w):
     return flops, kv_bytes, kv_bytes + io_bytes
 
 
+DECODE_SOURCES = ["mla_paged_kv_metadata_amd/csrc/mla_decode.hip", "mla_paged_kv_metadata_amd/csrc/mla_kernels.h"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_c2_hbm_traffic.json")
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the decode kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)
+        if rec.get("decode_source_hash") == decode_source_hash():
+            return int(rec["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_part):
+    """Average over dispatches of the kernel whose name contains name_part of
+    the counter's value summed over its instances (one dispatch = one id)."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", ""):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for a kernel named *{name_part}*")
+    return sum(per.values()) / len(per), len(per)
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, commands):
+    """Writes profiles/decode_c2_hbm_traffic.{md,json} from four rocprofv3 --pmc runs."""
+    copy_bytes = copy_mib << 20
+    cf, _ = _per_dispatch(_counter_rows(copy_fetch_dir), "FETCH_SIZE", "copy")
+    cw, _ = _per_dispatch(_counter_rows(copy_write_dir), "WRITE_SIZE", "copy")
+    df, nf = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE", "mla_decode_kernel")
+    dw, nw = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE", "mla_decode_kernel")
+    kf, kw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fetch_b, write_b = df * 1024 * kf, dw * 1024 * kw
+    w = None
+    from workloads import make_config
+    w = make_config(2)
+    _, kv_bytes, alg_bytes = work_counts(w)
+    rec = {"kernel": "mla_decode_kernel<bf16>", "workload": "standard MLA decode B=64 H=128 L~U[1024,4096]",
+           "decode_source_hash": decode_source_hash(),
+           "fetch_kib_per_dispatch": round(df, 1), "write_kib_per_dispatch": round(dw, 1),
+           "copy_mib": copy_mib, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
+           "hbm_bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "algorithmic_bytes_per_launch": alg_bytes, "kv_bytes_per_launch": kv_bytes,
+           "dispatches": {"fetch": nf, "write": nw}, "commands": commands}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    md = TRAFFIC_JSON[:-5] + ".md"
+    with open(md, "w") as fh:
+        fh.write("# HBM traffic of mla_decode_kernel<bf16>, standard decode B=64 H=128 L~U[1024,4096]\n\n")
+        fh.write("rocprofv3 TCC counters per dispatch (KiB, summed over instances), scaled by a plain "
+                 f"{copy_mib} MiB device copy measured the same way.\n\n")
+        fh.write("| quantity | value |\n|---|---|\n")
+        for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_kib", "copy_write_kib",
+                  "fetch_factor", "write_factor", "fetch_bytes", "write_bytes", "hbm_bytes_per_launch",
+                  "algorithmic_bytes_per_launch", "kv_bytes_per_launch", "decode_source_hash"):
+            fh.write(f"| {k} | {rec[k]} |\n")
+        fh.write(f"\nmeasured / algorithmic bytes: {rec['hbm_bytes_per_launch'] / alg_bytes:.3f}\n\n")
+        fh.write("Commands (from the repository root):\n\n")
+        for c in commands:
+            fh.write(f"    {c}\n")
+    print(open(md).read())
+
+
+def trace_summary(trace_dir, commands):
+    """Writes profiles/decode_c2_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(f[0], newline="")))
+    md = os.path.join(ROOT, "profiles", "decode_c2_kernel_trace.md")
+    with open(md, "w") as fh:
+        fh.write("# rocprofv3 kernel trace, standard decode B=64 H=128 L~U[1024,4096] (bench.py workload)\n\n")
+        fh.write("| kernel | calls | average us | min us | max us | share |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"]
+            if "mla" not in name and float(r["Percentage"]) < 1.0:
+                continue
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            fh.write(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |\n")
+        fh.write("\n(Other kernels are the harness's own copies and conversions outside the timed steps.)\n\n")
+        fh.write("Commands (from the repository root):\n\n")
+        for c in commands:
+            fh.write(f"    {c}\n")
+    print(open(md).read())
+
+
 def cpu_baseline(w, budget_s=20.0):
     """The fp64 oracle on the host cores over as many whole sequences as fit the budget."""
     from oracle import mla_decode as oracle_decode
@@ -80,9 +198,23 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="KV pool replicas rotated across steps")
     ap.add_argument("--num-parts", type=int, default=None, help="override the scheduler's balancing target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise four rocprofv3 --pmc output folders into profiles/ (no GPU work)")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy for --pmc-summary")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats folder into profiles/ (no GPU work)")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command line recorded in a --pmc-summary / --trace-summary file")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.copy_mib, args.pmc_command)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this decode path is built and "
               "measured on a single MI355X.", file=sys.stderr)
@@ -124,7 +256,6 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     K, W = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
 
     def step(i, events=None):
         kv = kvs[i % len(kvs)]
@@ -145,18 +276,53 @@ def main():
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+
+    # Timed region: K whole steps.  Each step's three launches are replayed from
+    # a HIP graph (one graph per KV replica), so the GPU runs them back to back
+    # without host launch gaps; --no-graph launches them eagerly instead.
+    timing = "eager"
+    graphs = []
+    if not args.no_graph:
+        try:
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for c in range(len(kvs)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
+                        step(c)
+                    graphs.append(g)
+            stream.wait_stream(side)
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            timing = "hip_graph"
+        except Exception as e:  # fall back to eager launches, and say so
+            log(f"graph capture failed ({e!r}); timing eager launches")
+            graphs = []
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(W + i, ev[i])
+        if graphs:
+            graphs[(W + i) % len(graphs)].replay()
+        else:
+            step(W + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
+
+    # Per-kernel durations: HIP events on the launch stream around each kernel
+    # of K eager steps (the decode kernel's average gives the roofline).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        step(W + i, ev[i])
+    torch.cuda.synchronize()
     t_meta = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
     t_dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
     t_cmb = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
     dec_s = float(t_dec.mean()) * 1e-3
-    log(f"step {ms_step * 1e3:.1f} us | metadata {t_meta.mean() * 1e3:.1f} us | decode {t_dec.mean() * 1e3:.1f} us "
-        f"(min {t_dec.min() * 1e3:.1f}) | combine {t_cmb.mean() * 1e3:.1f} us")
+    log(f"step {ms_step * 1e3:.1f} us ({timing}) | metadata {t_meta.mean() * 1e3:.1f} us | decode "
+        f"{t_dec.mean() * 1e3:.1f} us (min {t_dec.min() * 1e3:.1f}) | combine {t_cmb.mean() * 1e3:.1f} us")
 
     # correctness of the last step against the oracle on a few sequences
     check = {}
@@ -192,12 +358,14 @@ def main():
                                "L~U[1024,4096] seed 2, bf16 q/kv ~N(0,1), scale 1/24",
                    "batch": w.batch, "seq_len_q": w.s_q, "num_heads_q": w.num_heads_q,
                    "total_keys": int(w.cache_seqlens.sum()), "num_parts": P, "kv_copies": len(kvs)},
+        "timing": timing,
         "kv_gbps_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "kv_gbps_decode": round(kv_bytes / dec_s / 1e9, 1),
         "kernels_us": {"metadata": round(float(t_meta.mean()) * 1e3, 2),
                        "decode": round(float(t_dec.mean()) * 1e3, 2),
                        "combine": round(float(t_cmb.mean()) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "mla_decode_kernel<bf16>", "alg_bytes_per_launch": alg_bytes,
                      "kernel_tflops": round(flops / dec_s / 1e12, 1),
                      "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
