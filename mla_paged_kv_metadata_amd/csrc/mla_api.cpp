@@ -65,13 +65,10 @@ int check_heads(int batch, int heads_per_head_k, int num_heads_k) {
 
 int row_tiles(int rows) { return (rows + mla::kRowsPerTile - 1) / mla::kRowsPerTile; }
 
-// Per-split overhead in page units: loading the rows' q (rows x 1152 B) and
-// writing plus re-reading a bf16 partial with its lse (rows x 2 x 1028 B),
-// against a 73728-byte bf16 page.
-int default_fixed_cost(int rows) {
-  const long bytes = (long)rows * (1152 + 2 * 1028);
-  return (int)std::max(1L, (bytes + 36864) / 73728);
-}
+// Per-split overhead in page units: a split loads its rows' q and writes its
+// output rows (or a partial) on top of its pages; on MI355X that measured
+// about four bf16 pages for a 128-row tile and shrinks with fewer rows.
+int default_fixed_cost(int rows) { return std::max(1, std::min(rows, mla::kRowsPerTile) / 32); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -6,7 +6,8 @@
 // content.  The balancing rule is this library's own:
 //   sequence b costs fixed_cost + nblk_b units (nblk_b = ceil(L_b / 64));
 //   units of all sequences are laid end to end in batch order; part p owns
-//   units [p*W, (p+1)*W) with W = ceil(total / num_parts).  Part p works on
+//   units [floor(p*total/P), floor((p+1)*total/P)) (P = num_parts), so parts
+//   differ by at most one unit and none idles while total >= P.  Part p works on
 //   sequence b if it owns one of b's page units (or, when b has no pages, b's
 //   first unit); each such pair is one split of b, numbered k = 0, 1, ... in
 //   part order.
@@ -89,37 +90,42 @@ __global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restr
   __syncthreads();
   block_exclusive_scan(pref, B, tmp);
   const long long total = pref[B];
-  const long long W = max(1LL, ceil_div(total, num_parts));
+  const long long P = num_parts;
+  const long long W = max(1LL, ceil_div(total, P));          // most units of one part
+  auto bound = [&](long long p) -> long long { return p * total / P; };
+  auto part_of = [&](long long u) -> long long { return ((u + 1) * P - 1) / total; };   // u < total
 
+  // Splits of b = distinct parts owning its page units.  With total >= P every
+  // part owns a unit, so that is a difference of part indices; otherwise each
+  // unit is a part of its own.
   for (int b = tid; b < B; b += kT) {
     const long long nblk = pref[b + 1] - pref[b] - fc;
     const long long s = pref[b] + fc;                       // first page unit of b
-    cnt[b] = nblk > 0 ? (s + nblk - 1) / W - s / W + 1 : 1;
+    cnt[b] = nblk <= 0 ? 1 : (total >= P ? part_of(s + nblk - 1) - part_of(s) + 1 : nblk);
   }
   __syncthreads();
   block_exclusive_scan(cnt, B, tmp);
   for (int b = tid; b <= B; b += kT) num_splits[b] = (int32_t)cnt[b];
 
-  // Row p in closed form.  Part p owns units [pW, (p+1)W); it works on
-  // sequence b when it owns one of b's page units [s_b, s_b + nblk_b), or,
-  // for b without pages, b's first unit.  Its first sequence is the one
-  // holding unit pW or the next one; its last is the one holding its last
-  // unit or the one before.
-  auto works = [&](long long p, int b) -> bool {
-    const long long nblk = pref[b + 1] - pref[b] - fc, s = pref[b] + fc;
-    if (nblk > 0) return s + nblk > p * W && s < (p + 1) * W;
-    return pref[b] / W == p;
-  };
+  // Row p in closed form.  Part p works on sequence b when it owns one of
+  // b's page units [s_b, s_b + nblk_b), or, for b without pages, b's first
+  // unit.  Its first sequence is the one holding its first unit or the next
+  // one; its last is the one holding its last unit or the one before.
   for (int p = tid; p < num_parts; p += kT) {
     int32_t *row = tile_md + (size_t)p * 8;
-    const long long u0 = (long long)p * W, u1 = min((long long)(p + 1) * W, total);
+    const long long u0 = bound(p), u1 = bound(p + 1);
+    auto works = [&](int b) -> bool {
+      const long long nblk = pref[b + 1] - pref[b] - fc, s = pref[b] + fc;
+      if (nblk > 0) return s < u1 && s + nblk > u0;
+      return u0 <= pref[b] && pref[b] < u1;
+    };
     int b0 = -1, b1 = -1;
-    if (u0 < total) {
+    if (u0 < u1) {
       const int b = upper_index(pref, B, u0);
-      b0 = works(p, b) ? b : (b + 1 < B && works(p, b + 1) ? b + 1 : -1);
+      b0 = works(b) ? b : (b + 1 < B && works(b + 1) ? b + 1 : -1);
       if (b0 >= 0) {
         const int e = upper_index(pref, B, u1 - 1);
-        b1 = works(p, e) ? e : e - 1;
+        b1 = works(e) ? e : e - 1;
       }
     }
     row[5] = (int32_t)W;
@@ -130,11 +136,13 @@ __global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restr
     }
     const long long n0 = pref[b0 + 1] - pref[b0] - fc, s0 = pref[b0] + fc;
     const long long n1 = pref[b1 + 1] - pref[b1] - fc, s1 = pref[b1] + fc;
+    long long k0 = 0;
+    if (n0 > 0) k0 = total >= P ? p - part_of(s0) : max(u0, s0) - s0;
     row[0] = b0;
     row[1] = n0 > 0 ? (int32_t)max(0LL, u0 - s0) : 0;
     row[2] = b1;
-    row[3] = n1 > 0 ? (int32_t)min(n1, (long long)(p + 1) * W - s1) : 0;
-    row[4] = n0 > 0 ? (int32_t)(p - s0 / W) : 0;
+    row[3] = n1 > 0 ? (int32_t)min(n1, u1 - s1) : 0;
+    row[4] = (int32_t)k0;
     row[7] = b1 - b0 + 1;
   }
 }

@@ -9,7 +9,10 @@ units so the GPU scheduler kernel can be compared with it bit for bit:
   * Sequence b costs ``fixed_cost`` overhead units followed by one unit per
     page, nblk_b = ceil(L_b / page).  Units of all sequences are laid end to end
     in batch order; total = sum_b (fixed_cost + nblk_b).
-  * Payload W = ceil(total / num_parts).  Unit u belongs to part u // W.
+  * Part p owns units [floor(p * total / num_parts), floor((p+1) * total /
+    num_parts)): parts differ by at most one unit and none is left idle
+    while total >= num_parts.  W = ceil(total / num_parts) is the most units
+    a part owns.
   * Part p works on sequence b if it owns at least one of b's page units, or,
     for a sequence with no pages, if it owns b's first overhead unit.  Each
     such (part, sequence) pair is one split of b; the splits of b are numbered
@@ -44,10 +47,14 @@ def schedule(cache_seqlens, num_parts: int, fixed_cost: int, page: int = 64):
         units += [(b, j) for j in range(nblk[b])]
     total = len(units)
     W = max(1, -(-total // num_parts))
+    bounds = [p * total // num_parts for p in range(num_parts + 1)]
+    owner = []
+    for p in range(num_parts):
+        owner += [p] * (bounds[p + 1] - bounds[p])
     pages = [dict() for _ in range(num_parts)]   # pages[p][b] = ordered pages of b owned by p
     first_seen = set()
     for u, (b, j) in enumerate(units):
-        p = u // W
+        p = owner[u]
         if j >= 0:
             pages[p].setdefault(b, []).append(j)
         elif nblk[b] == 0 and b not in first_seen:
@@ -97,7 +104,8 @@ def check_schedule(tile_md, num_splits, cache_seqlens, num_parts, fixed_cost, pa
     Every page of every sequence is covered exactly once and in order by its
     splits, numbered k = 0, 1, ... in part order; every sequence gets >= 1
     split and num_splits counts them; total splits <= B + num_parts - 1; the
-    parts of one sequence's splits are consecutive; each part's real cost (its
+    parts of one sequence's splits increase with only idle parts between
+    them; each part's real cost (its
     pages plus fixed_cost per sequence whose pages it touches) is at most
     W + fixed_cost; idle rows are empty; the split count field is right.
     """
@@ -137,7 +145,10 @@ def check_schedule(tile_md, num_splits, cache_seqlens, num_parts, fixed_cost, pa
     for b in range(B):
         assert seen[b] == list(range(nblk[b])), b
         assert ks[b] == list(range(counts[b])), (b, ks[b], counts[b])
-        assert parts[b] == list(range(parts[b][0], parts[b][0] + len(parts[b]))), (b, parts[b])
+        # a sequence's parts increase, and any part between two of them is idle
+        for p0, p1 in zip(parts[b], parts[b][1:]):
+            assert p1 > p0, (b, parts[b])
+            assert all(md[q, 0] < 0 for q in range(p0 + 1, p1)), (b, parts[b])
     for p, c in cost.items():
         assert c <= W + fixed_cost, (p, c, W)
     return True

@@ -59,11 +59,18 @@ def test_hand_worked_two_part_table():
     md, ns = schedule([128, 256], 2, 1)
     assert ns.tolist() == [0, 1, 2]
     assert md.tolist() == [[0, 0, 0, 2, 0, 4, 1, 1], [1, 0, 1, 4, 0, 4, 1, 1]]
-    # W = 3 with three parts: part 0 = b0 whole; part 1 = b1's overhead + pages
-    # 0, 1; part 2 = b1's pages 2, 3.
+    # Three parts: boundaries floor(p * 8 / 3) = 0, 2, 5, 8.  Part 0 = units
+    # 0-1 (b0's overhead, page 0); part 1 = units 2-4 (b0's page 1, b1's
+    # overhead and page 0); part 2 = units 5-7 (b1's pages 1-3).
     md, ns = schedule([128, 256], 3, 1)
-    assert ns.tolist() == [0, 1, 3]
-    assert md.tolist() == [[0, 0, 0, 2, 0, 3, 1, 1], [1, 0, 1, 2, 0, 3, 1, 1], [1, 2, 1, 4, 1, 3, 1, 1]]
+    assert ns.tolist() == [0, 2, 4]
+    assert md.tolist() == [[0, 0, 0, 1, 0, 3, 1, 1], [0, 1, 1, 1, 1, 3, 1, 2], [1, 1, 1, 4, 1, 3, 1, 1]]
+    # More parts than units: boundaries floor(p * 2 / 5) = 0, 0, 0, 1, 1, 2, so
+    # part 2 owns the overhead unit (no page: it does not work on b0), part 4
+    # owns page 0, and the others own nothing.
+    md, ns = schedule([64], 5, 1)
+    assert ns.tolist() == [0, 1]
+    assert [r[0] for r in md.tolist()] == [-1, -1, -1, -1, 0]
 
 
 def test_long_sequence_is_spread_over_many_parts():
