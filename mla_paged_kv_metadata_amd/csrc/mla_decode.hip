@@ -455,6 +455,23 @@ __device__ __forceinline__ int lane_id_here() {
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
   return l;
 }
+// Row coordinates of this lane (row = 32-row wave tile + lane % 32, clamped
+// into range; query token qi and query head h of that row), re-derived from
+// an opaque lane index where they are needed rather than kept live across
+// the whole kernel.
+struct RowCoord {
+  int row, rowc, qi, h;
+};
+__device__ __forceinline__ RowCoord row_coord(int wrow0, int rows, int group, int hk) {
+  const int lane = lane_id_here();
+  RowCoord c;
+  c.row = wrow0 + (lane & 31);
+  c.rowc = min(c.row, rows - 1);
+  c.qi = c.rowc / group;
+  c.h = hk * group + (c.rowc - c.qi * group);
+  return c;
+}
+
 __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
                                            int nrows, LDS_AS uint8_t *stage) {
   const int lane = lane_id_here();
@@ -558,7 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   bf16x8 qf[kKSteps];
   // This lane's q fragments: row (qi, h) of sequence b, dims 16 ks + 8 hl .. +7.
   auto q_row = [&](int b) -> const uint16_t * {
-    return a.q + (((long)min(b, a.batch - 1) * a.s_q + qi) * a.hq + h) * kHeadDim + 8 * hl;
+    const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
+    return a.q + (((long)min(b, a.batch - 1) * a.s_q + c.qi) * a.hq + c.h) * kHeadDim + 8 * (lane_id_here() >> 5);
   };
   auto load_q = [&](int b) {
     const uint16_t *qrow = q_row(b);
@@ -681,6 +699,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
       }
     }
+    // The next split's q is loaded first, so its latency hides behind the
+    // epilogue (the next page's wait covers it).
+    if (b < b1) load_q(b + 1);
+
     // Epilogue.  A sequence with one split writes out / lse; otherwise the
     // split writes its normalised output (bf16) and lse to its partial slot,
     // which is its split number num_splits[b] + k.  The results are staged
@@ -692,19 +714,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const float inv = has ? 1.f / l : 0.f;
       const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
       const bool direct = nsplit <= 1;
-      const int prow = (slot * a.hk + hk) * a.rows + rowc;
-      const int orow = ((b * a.s_q + qi) * a.hq + h);
+      const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
+      const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
+      const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * (32 * kStageRow);
       store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow, wave_rows,
                  stage);
-      if (hl == 0 && row < a.rows) {
-        if (direct) a.lse[((long)b * a.hq + h) * a.s_q + qi] = lse_v;
+      if (lane_id_here() < 32 && c.row < a.rows) {
+        if (direct) a.lse[((long)b * a.hq + c.h) * a.s_q + c.qi] = lse_v;
         else a.part_lse[prow] = lse_v;
       }
     }
-    // The next split's q goes out after the stores (the next page's wait
-    // covers both).
-    if (b < b1) load_q(b + 1);
   }
 }
 
