@@ -23,10 +23,8 @@ struct DecodeArgs {
   float *lse;                 // [B][Hq][s_q]
   uint16_t *part_o;           // bf16 bits [slots][Hk][M][512], slots = batch + num_parts - 1
   float *part_lse;            // [slots][Hk][M]
-  int *arrivals;              // [B][Hk][row_tiles] split arrival counters (zero between calls)
   int batch, s_q, hq, hk, group, rows, max_blocks, row_tiles, num_parts, num_blocks;
   int kv_fp8, causal;
-  int fuse_combine;           // 1: the last split of a sequence to finish merges the partials
   float scale_log2;           // softmax_scale * log2(e)
   float v_scale;
 };
