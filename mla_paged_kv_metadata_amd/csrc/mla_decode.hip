@@ -586,15 +586,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
   int cur = 0;              // buffer that receives / holds the next page to process
   bool have_first = false;  // the first page of the current split is already in flight into it
+  // Block-table entries of a split are fetched one split ahead: lane i holds
+  // the page index of the split's page (first + i).
+  int bt_pref = 0;
   {
     // The part's first page goes out before its q, so both are in flight together.
     const int nblk0 = (seq_len(b0) + kPage - 1) / kPage;
     const int hi0 = seq_end(b0, nblk0), lo0 = max(0, min(md[1], hi0));
     if (hi0 > lo0) {
-      const uint8_t *src = page_addr(a.block_table[(long)b0 * a.max_blocks + lo0]);
+      const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
+      const uint8_t *src = page_addr(bt0[lo0]);
       if (kFp8) dma_page_fp8(page_src_fp8(src, tok_stride, wave, lane), stages[0], wave);
       else dma_page_bf16(page_src_bf16(src, tok_stride, wave, lane), bufs[0], wave);
       have_first = true;
+      bt_pref = bt0[min(lo0 + lane, nblk0 - 1)];
     }
   }
   load_q(b0);
@@ -615,10 +620,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     // while the last page of this split is processed.
     const uint8_t *next_src = kv_head;
     bool next_has_pages = false;
+    const int bt_this = bt_pref;                          // block-table lanes of this split (loaded earlier)
     if (b < b1) {
       const int Ln = seq_len(b + 1);
-      next_has_pages = seq_end(b + 1, (Ln + kPage - 1) / kPage) > 0;
-      if (next_has_pages) next_src = page_addr(a.block_table[(long)(b + 1) * a.max_blocks]);
+      const int nblk_n = (Ln + kPage - 1) / kPage;
+      next_has_pages = seq_end(b + 1, nblk_n) > 0;
+      if (next_has_pages) {
+        const int32_t *bt_n = a.block_table + (long)(b + 1) * a.max_blocks;
+        next_src = page_addr(bt_n[0]);
+        bt_pref = bt_n[min(lane, nblk_n - 1)];            // next split starts at page 0
+      }
     }
     if (tid == 0) *rerun_flag = 0;
 
@@ -634,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       // page index of j = bt_base + i, so a page lookup is a v_readlane instead
       // of a global-memory round trip per page; refilled every 64 pages.
       int bt_base = lo;
-      int bt_vec = bt[min(lo + lane, nblk - 1)];
+      int bt_vec = bt_this;
       auto page_of = [&](int j) -> int {
         if ((unsigned)(j - bt_base) >= 64u) {        // uniform; also on a re-run from lo
           bt_base = j;
