@@ -234,10 +234,16 @@ __device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_
 // score exceeds the first keys' maximum by 64/log2(e) ~ 44 natural-log units.
 constexpr float kRefSlackLog2 = 64.0f;
 
-// c + 0 * 0 on the matrix core: produces zeroed accumulators in the MFMA
-// accumulation registers.
-__device__ __forceinline__ f32x16 mfma_zero() {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{}, bf16x8{}, f32x16{}, 0, 0, 0);
+// c + 0 * 0 on the matrix core: zeroes all O^T accumulators in the MFMA
+// accumulation registers.  The zero operand comes from an opaque move at the
+// point of use; a plain constant would be hoisted out of the sequence loop,
+// where it would only occupy (or spill) four VGPRs between uses.
+__device__ __forceinline__ void mfma_zero_all(f32x16 (&o)[kOTiles]) {
+  unsigned z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  const bf16x8 zz = __builtin_bit_cast(bf16x8, u32x4{z, z, z, z});
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zz, zz, f32x16{}, 0, 0, 0);
 }
 
 // S^T accumulation steps on the matrix core with the accumulator pinned to
@@ -433,18 +439,21 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 
 // Writes this wave's 32 x 512 result rows (times f, rounded to bf16) to
 // global memory, coalesced: the O^T accumulators hold one row per lane and
-// 4-dim pieces, so the tile is transposed through LDS (`stage`, 32 rows of
-// 528 bytes per wave, private to the wave) in two rounds of 256 dims.  Per
-// round, pairs of 4-dim pieces are merged into 16-byte chunks across
-// lane ^ 32 with v_permlane32_swap; the 16-byte row padding makes both the
-// column writes (16 rows, one chunk) and the row reads (one row, 16 chunks)
-// conflict-free.  Each read-back instruction covers two whole 512-byte half
-// rows, which go out as one contiguous 16-byte store per lane.
+// 4-dim pieces, so the tile is transposed through LDS (`stage`, private to
+// the wave) in four rounds of 128 dims that alternate between two 32-row
+// regions, so one round's read-back and stores overlap the next round's
+// conversion.  Per round, pairs of 4-dim pieces are merged into 16-byte
+// chunks across lane ^ 32 with v_permlane32_swap; the 16-byte row padding
+// makes both the column writes (16 rows, one chunk) and the row reads (one
+// row, 16 chunks) conflict-free.  Each read-back instruction covers four
+// 256-byte row pieces, which go out as one contiguous 16-byte store per lane.
 //   row_idx : this lane's destination row index in units of 512 elements
 //             (lanes 0..31 hold rows 0..31 of the wave)
 //   nrows   : number of valid rows of the wave (0..32)
-constexpr int kStageRow = 528;
-static_assert(4 * 32 * kStageRow <= kPageBytes, "the four waves' staging fits in one page buffer");
+constexpr int kStageRow = 272;                     // 128 dims (256 B) + 16 B padding
+constexpr int kStageRegion = 32 * kStageRow;       // one round's rows
+constexpr int kStageWave = 2 * kStageRegion;       // two alternating regions per wave
+static_assert(4 * kStageWave <= kPageBytes, "the four waves' staging fits in one page buffer");
 // The lane index is re-derived here through an opaque instruction: the
 // lane-dependent addresses below are then computed where they are used
 // instead of being hoisted out of the sequence loop, where they would only
@@ -475,14 +484,14 @@ __device__ __forceinline__ RowCoord row_coord(int wrow0, int rows, int group, in
 __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
                                            int nrows, LDS_AS uint8_t *stage) {
   const int lane = lane_id_here();
-  const int r = lane & 31, hl = lane >> 5, c = lane & 31;
-  LDS_AS uint8_t *wr = stage + r * kStageRow + (hl ? 0 : 16);    // lanes < 32 write the odd chunk of a pair
-  const LDS_AS uint8_t *rd = stage + hl * kStageRow + c * 16;    // row 2k + hl, chunk c
+  const int r = lane & 31, hl = lane >> 5, g = lane >> 4, c = lane & 15;
 #pragma unroll
-  for (int R = 0; R < 2; ++R) {
+  for (int R = 0; R < 4; ++R) {
+    LDS_AS uint8_t *region = stage + (R & 1) * kStageRegion;
+    LDS_AS uint8_t *wr = region + r * kStageRow + (hl ? 0 : 16);   // lanes < 32 write the odd chunk of a pair
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int t = 8 * R + tt;
+    for (int tt = 0; tt < 4; ++tt) {
+      const int t = 4 * R + tt;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         // piece q holds dims 8q + 4*hl .. +3 of tile t
@@ -496,21 +505,17 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, 
         *(LDS_AS u32x4 *)(wr + (4 * tt + 2 * pp) * 16) = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
     }
-    // Read-backs in batches of 8 (their latencies overlap), then the stores.
-    // Row validity is tested per row pair with wave-uniform branches.
+    // Read-backs (row 4k + g, chunk c), then the stores.
+    const LDS_AS uint8_t *rd = region + g * kStageRow + c * 16;
+    u32x4 v[8];
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 8) {
-      u32x4 v[8];
+    for (int k = 0; k < 8; ++k) v[k] = *(const LDS_AS u32x4 *)(rd + 4 * k * kStageRow);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = *(const LDS_AS u32x4 *)(rd + 2 * (k0 + k) * kStageRow);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int rr = 2 * (k0 + k);
-        const int ra = __builtin_amdgcn_readlane(row_idx, rr), rb = __builtin_amdgcn_readlane(row_idx, rr + 1);
-        uint16_t *dst = base + (long)(hl ? rb : ra) * kHeadDimV + R * 256 + c * 8;
-        if (rr + 1 < nrows) *(u32x4 *)dst = v[k];
-        else if (rr < nrows && hl == 0) *(u32x4 *)dst = v[k];
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + g;
+      const int dst_row = __shfl(row_idx, rr, 64);
+      uint16_t *dst = base + (long)dst_row * kHeadDimV + R * 128 + c * 8;
+      if (rr < nrows) *(u32x4 *)dst = v[k];
     }
   }
 }
@@ -552,11 +557,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int wrow0 = rt * kRowsPerTile + wave * 32;
   const bool active = wrow0 < a.rows;                 // wave-uniform
   const int wave_rows = max(0, min(32, a.rows - wrow0));
-  const int row = wrow0 + (lane & 31);
-  const int rowc = min(row, a.rows - 1);              // rows past `rows` compute a valid row, never stored
-  const int qi = rowc / a.group;                      // query token of this row
-  const int h = hk * a.group + (rowc - qi * a.group); // query head of this row
-  const int hl = lane >> 5;
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
 
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int first_slot = a.num_splits[b];
     const int nsplit = a.num_splits[b + 1] - first_slot;
     const int slot = max(0, min(first_slot + (b == b0 ? md[4] : 0), nslots - 1));
-    const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + qi)) : L;
+    const int nvis = a.causal ? max(0, min(L, L - a.s_q + 1 + row_coord(wrow0, a.rows, a.group, hk).qi)) : L;
     // Smallest visible-key count of the workgroup (its first query token sees
     // the fewest keys): pages at or past it need per-key masking.
     const int nvis_min = a.causal ? max(0, min(L, L - a.s_q + 1 + qi_min)) : L;
@@ -637,8 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     // O^T accumulators start as the result of an all-zero MFMA so that they
     // live in accumulation registers from the first page on.
     f32x16 o[kOTiles];
-#pragma unroll
-    for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+    mfma_zero_all(o);
 
     if (hi > lo) {
       // Block-table entries of the split live in one VGPR, lane i holding the
@@ -706,8 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         if (m_restart != kNegInf) m = m_restart;
         m_restart = kNegInf;
         l = 0.f;
-#pragma unroll
-        for (int t = 0; t < kOTiles; ++t) o[t] = mfma_zero();
+        mfma_zero_all(o);
       }
     }
     // The next split's q is loaded first, so its latency hides behind the
@@ -728,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
-      LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * (32 * kStageRow);
+      LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * kStageWave;
       store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow, wave_rows,
                  stage);
       if (lane_id_here() < 32 && c.row < a.rows) {
