@@ -139,8 +139,9 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, 
     print(open(md).read())
 
 
-def trace_summary(trace_dir, commands):
-    """Writes profiles/decode_c2_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder."""
+def trace_summary(trace_dir, commands, bench_json=None):
+    """Writes profiles/decode_c2_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder
+    (and, if given, the JSON line that the profiled bench run printed)."""
     import csv
     import glob
     f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -159,6 +160,12 @@ def trace_summary(trace_dir, commands):
             fh.write(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |\n")
         fh.write("\n(Other kernels are the harness's own copies and conversions outside the timed steps.)\n\n")
+        if bench_json:
+            with open(bench_json) as bj:
+                rec = json.loads(bj.read().strip().splitlines()[-1])
+            fh.write("Per-kernel averages that the profiled run measured itself with HIP events (us): "
+                     + ", ".join(f"{k} {v}" for k, v in rec["kernels_us"].items())
+                     + f"; step {rec['ms_per_step'] * 1e3:.1f} us.\n\n")
         fh.write("Commands (from the repository root):\n\n")
         for c in commands:
             fh.write(f"    {c}\n")
@@ -201,8 +208,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (2, the standard B=64 H=128 decode, is the headline; others for reference)")
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--copies", type=int, default=4, help="KV pool replicas rotated across steps")
     ap.add_argument("--num-parts", type=int, default=None, help="override the scheduler's balancing target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,6 +221,7 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy for --pmc-summary")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats folder into profiles/ (no GPU work)")
+    ap.add_argument("--bench-json", help="the profiled run's JSON line, quoted in a --trace-summary file")
     ap.add_argument("--pmc-command", action="append", default=[],
                     help="command line recorded in a --pmc-summary / --trace-summary file")
     args = ap.parse_args()
@@ -221,7 +229,7 @@ def main():
         pmc_summary(*args.pmc_summary, args.copy_mib, args.pmc_command)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.pmc_command)
+        trace_summary(args.trace_summary, args.pmc_command, args.bench_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this decode path is built and "
@@ -273,29 +281,23 @@ def main():
     stream = torch.cuda.current_stream(dev)
     K, W = args.steps, args.warmup
 
-    def step(i, events=None):
+    def step(i):
         kv = kvs[i % len(kvs)]
-        if events:
-            events[0].record(stream)
         mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, tile_md=md, num_splits=ns)
-        if events:
-            events[1].record(stream)
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
                            lse=lse, workspace=ws, stage="splits")
-        if events:
-            events[2].record(stream)
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
                            lse=lse, workspace=ws, stage="combine")
-        if events:
-            events[3].record(stream)
 
-    for i in range(W):
+    for i in range(2):                      # first launches (library and allocator set-up)
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps.  Each step's three launches are replayed from
-    # a HIP graph (one graph per KV replica), so the GPU runs them back to back
-    # without host launch gaps; --no-graph launches them eagerly instead.
+    # Each step's three launches are replayed from a HIP graph (one graph per KV
+    # replica), so the GPU runs them back to back without host launch gaps;
+    # --no-graph launches them eagerly instead.  The W warm-up steps run the
+    # same way: under sustained load the GPU takes some 20 ms to reach its
+    # steady clock, so the default W covers about 50 ms of steps.
     timing = "eager"
     graphs = []
     if not args.no_graph:
@@ -309,14 +311,18 @@ def main():
                         step(c)
                     graphs.append(g)
             stream.wait_stream(side)
-            for g in graphs:
-                g.replay()
             torch.cuda.synchronize()
             timing = "hip_graph"
         except Exception as e:  # fall back to eager launches, and say so
             log(f"graph capture failed ({e!r}); timing eager launches")
             graphs = []
+    for i in range(W):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
     torch.cuda.synchronize()
+    # Timed region: K whole steps.
     t0 = time.perf_counter()
     for i in range(K):
         if graphs:
@@ -327,18 +333,55 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
 
-    # Per-kernel durations: HIP events on the launch stream around each kernel
-    # of K eager steps (the decode kernel's average gives the roofline).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for i in range(K):
-        step(W + i, ev[i])
+    # Per-kernel durations: each kernel alone, K launches back to back (graph-
+    # replayed like the steps, else eager), bracketed by HIP events on the
+    # launch stream; the average launch of the decode kernel gives the roofline.
+    def meta_call(i):
+        mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, tile_md=md, num_splits=ns)
+
+    def decode_call(i):
+        mla.mla_decode_fwd(q, kvs[i % len(kvs)], bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2,
+                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="splits")
+
+    def combine_call(i):
+        mla.mla_decode_fwd(q, kvs[i % len(kvs)], bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2,
+                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="combine")
+
+    def kernel_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if graphs:
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(K):
+                        fn(W + i)
+            stream.wait_stream(side)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        else:
+            for i in range(2):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(K):
+                fn(W + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    t_meta_us, t_dec_us, t_cmb_us = kernel_us(meta_call), kernel_us(decode_call), kernel_us(combine_call)
+    # The outputs checked below come from whole steps.
+    for i in range(len(kvs)):
+        step(i)
     torch.cuda.synchronize()
-    t_meta = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    t_dec = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
-    t_cmb = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
-    dec_s = float(t_dec.mean()) * 1e-3
-    log(f"step {ms_step * 1e3:.1f} us ({timing}) | metadata {t_meta.mean() * 1e3:.1f} us | decode "
-        f"{t_dec.mean() * 1e3:.1f} us (min {t_dec.min() * 1e3:.1f}) | combine {t_cmb.mean() * 1e3:.1f} us")
+    dec_s = t_dec_us * 1e-6
+    log(f"step {ms_step * 1e3:.1f} us ({timing}) | metadata {t_meta_us:.1f} us | decode {t_dec_us:.1f} us | "
+        f"combine {t_cmb_us:.1f} us")
 
     # correctness of the last step against the oracle on a few sequences
     check = {}
@@ -398,9 +441,8 @@ def main():
         "timing": timing,
         "kv_gbps_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_gbps_decode": round(kv_bytes / dec_s / 1e9, 1),
-        "kernels_us": {"metadata": round(float(t_meta.mean()) * 1e3, 2),
-                       "decode": round(float(t_dec.mean()) * 1e3, 2),
-                       "combine": round(float(t_cmb.mean()) * 1e3, 2)},
+        "kernels_us": {"metadata": round(t_meta_us, 2), "decode": round(t_dec_us, 2),
+                       "combine": round(t_cmb_us, 2)},
         "roofline": roof,
         "check": check,
     }
