@@ -262,8 +262,6 @@ __device__ __forceinline__ void mfma_qk(f32x16 &s, const bf16x8 &a, const bf16x8
 __device__ __forceinline__ void mfma_qk_drain(f32x16 &s) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s));
 }
-// Orders a second accumulator after mfma_qk_drain (whose wait states cover it).
-__device__ __forceinline__ void mfma_qk_drain_short(f32x16 &s) { asm("" : "+v"(s)); }
 
 // Exchange with lane ^ 32 through v_permlane32_swap (no LDS round trip):
 // swapping a value with itself leaves the lower-half copy in r[0] and the
@@ -335,93 +333,127 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
     hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
   };
 
-  // S^T = K Q^T for both 32-token tiles: two independent accumulation chains
-  // interleaved, so a dependent MFMA never waits on its predecessor.
-  constexpr int kPre = 2;                              // k-steps in flight (2 fragments each)
-  bf16x8 k0[kPre], k1[kPre];
+  // Online softmax of one 32-token tile, in kSoftPieces pieces that are
+  // placed between matrix-core instructions of the other tile, so the VALU
+  // work runs while the matrix core computes.  In S^T a lane holds head r and
+  // tokens (i/4)*8 + 4*hl + i%4 (s[i]) of the tile.  Tiles are independent:
+  // O and l share the fixed reference m, so nothing is rescaled; the first
+  // tile with a visible key fixes m.
+  //   pieces 0-1: mask the scores of invisible keys (8 each)
+  //   pieces 2-5: running max over 4 scores each
+  //   piece 6   : max across the lane halves, reference update, re-run flag
+  //   pieces 7-14: probabilities exp2(s * scale_log2 - m), 2 each, and their sum
+  //   piece 15  : P^T as bf16 (k-steps 2*tile and 2*tile + 1)
+  //   piece 16  : row sum across the lane halves into l
+  float mx = kNegInf, ps = 0.f, mu = 0.f;
+  bool need = false;
+  auto soft = [&](f32x16 &sc, bf16x8 &p_lo, bf16x8 &p_hi, int tok0, int piece) {
+    if (piece < 2) {
+      if (mask) {
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    k0[i] = kload(i, 0);
-    k1[i] = kload(i, 1);
-  }
+        for (int i = 8 * piece; i < 8 * piece + 8; ++i) {
+          const int tok = tok0 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          if (tok >= nvis) sc[i] = kNegInf;
+        }
+      }
+    } else if (piece < 6) {
+      const int i0 = 4 * (piece - 2);
+      const float t = fmaxf(fmaxf(sc[i0], sc[i0 + 1]), fmaxf(sc[i0 + 2], sc[i0 + 3]));
+      mx = piece == 2 ? t : fmaxf(mx, t);
+    } else if (piece == 6) {
+      float t = max_across_halves(mx);
+      t = (t == kNegInf) ? kNegInf : t * scale_log2;
+      if (m == kNegInf) m = t;                          // first visible keys fix the reference
+      const bool nd = t > m + kRefSlackLog2;
+      if (nd) m_restart = fmaxf(m_restart, t);
+      need |= nd;
+      mu = (m == kNegInf) ? 0.f : m;
+    } else if (piece < 15) {
+      const int i0 = 2 * (piece - 7);
+      sc[i0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0], scale_log2, -mu));
+      sc[i0 + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0 + 1], scale_log2, -mu));
+      ps = (piece == 7 ? 0.f : ps) + (sc[i0] + sc[i0 + 1]);
+    } else if (piece == 15) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p_lo[e] = (__bf16)sc[e];
+        p_hi[e] = (__bf16)sc[8 + e];
+      }
+    } else {
+      l += sum_across_halves(ps);
+    }
+  };
+  constexpr int kSoftPieces = 17;
+
+  // S^T = K Q^T, one 32-token tile after the other: step g runs k-step g % 36
+  // of tile g / 36 (a single accumulation chain per tile; the matrix core
+  // forwards an accumulator to the next MFMA of its chain).  K operands are
+  // prefetched kPre steps ahead; the tile-0 softmax runs under the tile-1
+  // chain.
+  constexpr int kPre = 4;
+  constexpr int kDmaEvery = 2 * kKSteps / (kFp8 ? kF8PageLoads : kPageLoads);   // 4 (bf16) or 8 (fp8)
+  bf16x8 kf[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) kf[i] = kload(i, 0);
   __builtin_amdgcn_sched_barrier(0);
   f32x16 s0, s1;
+  bf16x8 pb[4];              // P^T operand for PV k-step ks: tile ks/2, scores 8*(ks%2) .. +7
+  // One step of a tile's chain: MFMA, the operand kPre steps ahead (crossing
+  // into tile 1 at the end of tile 0), and every kDmaEvery-th step one copy
+  // instruction of the next page.
+  auto qk_step = [&](f32x16 &sc, int tile, int ks) {
+    const int g = tile * kKSteps + ks, sl = g % kPre;
+    if (ks == 0) mfma_qk_first(sc, kf[sl], qf[0]);
+    else mfma_qk(sc, kf[sl], qf[ks]);
+    if (g + kPre < 2 * kKSteps) kf[sl] = kload((g + kPre) % kKSteps, (g + kPre) / kKSteps);
+    if (nx.valid && g % kDmaEvery == 0) {
+      if (kFp8) dma_fp8_dispatch(nx.src, nx.dst, nx.wave, g / kDmaEvery);
+      else dma_bf16_dispatch(nx.src, nx.dst, nx.wave, g / kDmaEvery);
+    }
+  };
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
-    const int sl = ks % kPre;
-    if (ks == 0) {
-      mfma_qk_first(s0, k0[sl], qf[0]);
-      mfma_qk_first(s1, k1[sl], qf[0]);
-    } else {
-      mfma_qk(s0, k0[sl], qf[ks]);
-      mfma_qk(s1, k1[sl], qf[ks]);
-    }
-    if (ks + kPre < kKSteps) {
-      k0[sl] = kload(ks + kPre, 0);
-      k1[sl] = kload(ks + kPre, 1);
-    }
-    // One copy instruction every other k-step (denser issue stalls the
-    // matrix core more than it gains).
-    if (nx.valid && (ks & 1) == 0 && ks / 2 < (kFp8 ? kF8PageLoads : kPageLoads)) {
-      if (kFp8) dma_fp8_dispatch(nx.src, nx.dst, nx.wave, ks / 2);
-      else dma_bf16_dispatch(nx.src, nx.dst, nx.wave, ks / 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);                 // keep loads kPre k-steps ahead
+    qk_step(s0, 0, ks);
+    __builtin_amdgcn_sched_barrier(0);                 // keep loads kPre steps ahead
   }
-  // First V^T operands load while the softmax runs.
+  // Tile 1, with tile 0's softmax pieces over its steps 1 .. kKSteps - 2.
+  constexpr int kSoftBN = kKSteps - 2;
+  static_assert(kSoftPieces <= kSoftBN && kSoftPieces <= 2 * kOTiles - 2, "one piece per step at most");
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    qk_step(s1, 1, ks);
+    if (ks == 0) mfma_qk_drain(s0);                    // tile 0's last MFMA -> first VALU read
+    const int j = ks - 1;
+    if (j >= 0 && j < kSoftBN && (j + 1) * kSoftPieces / kSoftBN != j * kSoftPieces / kSoftBN)
+      soft(s0, pb[0], pb[1], key0, j * kSoftPieces / kSoftBN);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // First V^T operands.
   constexpr int kVPre = 4;
   bf16x4 vlo[kVPre], vhi[kVPre];
 #pragma unroll
   for (int i = 0; i < kVPre; ++i) vload(i, vlo[i], vhi[i]);
-  mfma_qk_drain(s0);
-  mfma_qk_drain_short(s1);
 
-  // Online softmax over this page's 64 keys: lane holds head r, tokens
-  // (i/4)*8 + 4*hl + i%4 of tile 0 (s0[i]) and 32 + the same of tile 1 (s1[i]).
-  if (mask) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = key0 + (i >> 2) * 8 + hl * 4 + (i & 3);
-      if (tok >= nvis) s0[i] = kNegInf;
-      if (tok + 32 >= nvis) s1[i] = kNegInf;
-    }
-  }
-  float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-  mx = max_across_halves(mx);
-  mx = (mx == kNegInf) ? kNegInf : mx * scale_log2;
-  if (m == kNegInf) m = mx;                           // first visible keys fix the reference
-  const bool need = mx > m + kRefSlackLog2;
-  if (need) m_restart = fmaxf(m_restart, mx);
-  const float mu = (m == kNegInf) ? 0.f : m;
-  float ps = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], scale_log2, -mu));
-    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], scale_log2, -mu));
-    ps += s0[i] + s1[i];
-  }
-  l += sum_across_halves(ps);
-
-  // P^T operand for k-step ks: tile ks/2, score registers 8*(ks%2) .. +7.
-  bf16x8 pb[4];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    pb[0][e] = (__bf16)s0[e];
-    pb[1][e] = (__bf16)s0[8 + e];
-    pb[2][e] = (__bf16)s1[e];
-    pb[3][e] = (__bf16)s1[8 + e];
-  }
-
-  // O^T += V^T P^T over 4 k-steps x 16 dim tiles.
-#pragma unroll
-  for (int step = 0; step < 4 * kOTiles; ++step) {
+  // O^T += V^T P^T over 4 k-steps x 16 dim tiles; the tile-1 softmax runs
+  // under the first two k-steps (tile 0's P), which do not need it.
+  auto pv_step = [&](int step) {
     const int sl = step % kVPre;
     const bf16x8 av = __builtin_shufflevector(vlo[sl], vhi[sl], 0, 1, 2, 3, 4, 5, 6, 7);
     o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[step >> 4], o[step & 15], 0, 0, 0);
     if (step + kVPre < 4 * kOTiles) vload(step + kVPre, vlo[sl], vhi[sl]);
+  };
+  constexpr int kSoftCN = 2 * kOTiles - 2;
+#pragma unroll
+  for (int step = 0; step < 2 * kOTiles; ++step) {
+    pv_step(step);
+    if (step == 0) mfma_qk_drain(s1);                  // tile 1's last MFMA -> first VALU read
+    const int j = step - 1;
+    if (j >= 0 && j < kSoftCN && (j + 1) * kSoftPieces / kSoftCN != j * kSoftPieces / kSoftCN)
+      soft(s1, pb[2], pb[3], key0 + 32, j * kSoftPieces / kSoftCN);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int step = 2 * kOTiles; step < 4 * kOTiles; ++step) pv_step(step);
   return __ballot(need) != 0;
 }
 
