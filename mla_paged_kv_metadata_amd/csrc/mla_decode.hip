@@ -622,19 +622,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   // the page index of the split's page (first + i).
   int bt_pref = 0;
   {
-    // The part's first page goes out before its q, so both are in flight together.
-    const int nblk0 = (seq_len(b0) + kPage - 1) / kPage;
-    const int hi0 = seq_end(b0, nblk0), lo0 = max(0, min(md[1], hi0));
-    if (hi0 > lo0) {
-      const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
-      const uint8_t *src = page_addr(bt0[lo0]);
+    // The part's first block-table entries and length load together, and
+    // its q goes out while they are in flight; then its first page.  (Lanes
+    // past the split's pages hold entries that are never used; the index is
+    // clamped into the table row.)
+    const int first0 = max(0, md[1]);
+    const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
+    bt_pref = bt0[min(first0 + lane, a.max_blocks - 1)];
+    const int len0 = seq_len(b0);
+    load_q(b0);
+    const int nblk0 = (len0 + kPage - 1) / kPage;
+    const int hi0 = seq_end(b0, nblk0);
+    if (hi0 > first0) {                               // then the split's first page is first0
+      const uint8_t *src = page_addr(__builtin_amdgcn_readfirstlane(bt_pref));
       if (kFp8) dma_page_fp8(page_src_fp8(src, tok_stride, wave, lane), stages[0], wave);
       else dma_page_bf16(page_src_bf16(src, tok_stride, wave, lane), bufs[0], wave);
       have_first = true;
-      bt_pref = bt0[min(lo0 + lane, nblk0 - 1)];
     }
   }
-  load_q(b0);
   for (int b = b0; b <= b1; ++b) {
     const int L = seq_len(b);
     const int nblk = (L + kPage - 1) / kPage;
