@@ -496,6 +496,14 @@ __device__ __forceinline__ int lane_id_here() {
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
   return l;
 }
+// The same for a wave-uniform value: an opaque scalar copy, so that values
+// derived from it are computed where used rather than kept live (in VGPRs)
+// across the sequence loop.
+__device__ __forceinline__ int uniform_here(int v) {
+  int r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+  return r;
+}
 // Row coordinates of this lane (row = 32-row wave tile + lane % 32, clamped
 // into range; query token qi and query head h of that row), re-derived from
 // an opaque lane index where they are needed rather than kept live across
@@ -537,17 +545,25 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, 
         *(LDS_AS u32x4 *)(wr + (4 * tt + 2 * pp) * 16) = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
     }
-    // Read-backs (row 4k + g, chunk c), then the stores.
+    // Read-backs (row 4k + g, chunk c) and the rows' destinations, then the
+    // stores; a full tile takes a branch-free path, so that the LDS reads and
+    // lane exchanges go out together and are awaited once.
     const LDS_AS uint8_t *rd = region + g * kStageRow + c * 16;
     u32x4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = *(const LDS_AS u32x4 *)(rd + 4 * k * kStageRow);
+    int dst_row[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int rr = 4 * k + g;
-      const int dst_row = __shfl(row_idx, rr, 64);
-      uint16_t *dst = base + (long)dst_row * kHeadDimV + R * 128 + c * 8;
-      if (rr < nrows) *(u32x4 *)dst = v[k];
+      v[k] = *(const LDS_AS u32x4 *)(rd + 4 * k * kStageRow);
+      dst_row[k] = __builtin_amdgcn_ds_bpermute((4 * k + g) << 2, row_idx);
+    }
+    uint16_t *col = base + R * 128 + c * 8;
+    if (nrows == 32) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) *(u32x4 *)(col + (long)dst_row[k] * kHeadDimV) = v[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (4 * k + g < nrows) *(u32x4 *)(col + (long)dst_row[k] * kHeadDimV) = v[k];
     }
   }
 }
@@ -588,7 +604,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
   const int wrow0 = rt * kRowsPerTile + wave * 32;
   const bool active = wrow0 < a.rows;                 // wave-uniform
-  const int wave_rows = max(0, min(32, a.rows - wrow0));
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
 
@@ -764,7 +779,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * kStageWave;
-      store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow, wave_rows,
+      store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow,
+                 max(0, min(32, uniform_here(a.rows) - wrow0)),
                  stage);
       if (lane_id_here() < 32 && c.row < a.rows) {
         if (direct) a.lse[((long)b * a.hq + c.h) * a.s_q + c.qi] = lse_v;
