@@ -19,12 +19,15 @@ What it follows (page titles as cited everywhere in this repository):
   * FlashInfer ``trtllm_batch_decode_with_kv_cache_mla`` page: query is
     q_nope ++ q_rope (512 + 64), kv_cache is ckv ++ kpe, so V = the first 512
     (kv_lora_rank) columns; note on fused scales
-    bmm1 = q_scale*k_scale*sm_scale/sqrt(head_dim_qk), bmm2 = v_scale*o_scale.
+    bmm1 = q_scale*k_scale*sm_scale/sqrt(head_dim_qk), bmm2 = v_scale*o_scale;
+    ``sinks``, a per-head extra term of the softmax denominator.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): natural-log lse with the scale inside the exponent; bottom-right
 causal alignment (query i of s_q sees keys t < L - s_q + 1 + i); a row with no
-visible key gives out = 0 and lse = -inf; q head h uses KV head h // (H_q/H_k).
+visible key gives out = 0 and lse = -inf; q head h uses KV head h // (H_q/H_k);
+a sink is a logit on the scale of softmax_scale * q.k, so head h's softmax
+denominator gains exp(sink_h) (no value row goes with it) and lse includes it.
 """
 from __future__ import annotations
 
@@ -98,22 +101,37 @@ def gather_rows(kv: np.ndarray, block_table_row: np.ndarray, L: int, page_block_
     return np.concatenate(pages, axis=0)[:L]
 
 
-def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, v_scale: float = 1.0):
+def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, v_scale: float = 1.0, sink=None):
     """Softmax attention of query rows qh (G, D) over keys K (n, D), values V (n, Dv).
 
     Returns (out (G, Dv), lse (G,)) with lse = ln sum_j exp(scale * q.k_j).
-    n == 0 gives out = 0, lse = -inf.
+    n == 0 gives out = 0, lse = -inf.  With ``sink`` (G,) (FlashInfer MLA
+    page, ``sinks``: a per-head extra term of the softmax denominator, read as
+    a logit): the denominator is sum_j exp(s_j) + exp(sink), lse includes the
+    sink term, and the sink carries no value.  A sink of -inf is no sink.
     """
     G = qh.shape[0]
     n = K.shape[0]
-    if n == 0:
-        return np.zeros((G, V.shape[1])), np.full(G, -np.inf)
-    s = scale * (qh @ K.T)                      # (G, n)
-    mx = s.max(axis=1, keepdims=True)
+    if sink is None:
+        if n == 0:
+            return np.zeros((G, V.shape[1])), np.full(G, -np.inf)
+        s = scale * (qh @ K.T)                  # (G, n)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        Z = e.sum(axis=1, keepdims=True)
+        out = v_scale * (e @ V) / Z
+        lse = (mx + np.log(Z))[:, 0]
+        return out, lse
+    sink = np.asarray(sink, dtype=np.float64).reshape(G, 1)
+    s = scale * (qh @ K.T) if n else np.zeros((G, 0))
+    mx = np.maximum(s.max(axis=1, keepdims=True) if n else np.full((G, 1), -np.inf), sink)
+    empty = ~np.isfinite(mx)                    # no key and no sink: out = 0, lse = -inf
+    mx = np.where(empty, 0.0, mx)
     e = np.exp(s - mx)
-    Z = e.sum(axis=1, keepdims=True)
-    out = v_scale * (e @ V) / Z
-    lse = (mx + np.log(Z))[:, 0]
+    Z = e.sum(axis=1, keepdims=True) + np.exp(sink - mx)
+    Zs = np.where(empty, 1.0, Z)
+    out = np.where(empty, 0.0, v_scale * (e @ V[:n]) / Zs)
+    lse = np.where(empty, -np.inf, mx + np.log(Zs))[:, 0]
     return out, lse
 
 
@@ -138,13 +156,14 @@ def lse_merge(outs, lses):
 
 
 def mla_decode_f64(q: np.ndarray, rows_of, cache_seqlens, num_heads_k: int, head_dim_v: int,
-                   softmax_scale: float, causal: bool, v_scale: float = 1.0, batches=None):
+                   softmax_scale: float, causal: bool, v_scale: float = 1.0, batches=None, sinks=None):
     """Core oracle on float64 operands.
 
     q: (B, s_q, H_q, D) float64.  rows_of(b) -> (L_b, H_k, D) float64, the
     sequence's cached rows in logical order.  Returns out (B, s_q, H_q, Dv) and
     lse (B, H_q, s_q) float64.  ``batches`` restricts the work to some b (the
-    other entries stay 0 / -inf).
+    other entries stay 0 / -inf).  ``sinks``: None or (H_q,) per-head sink
+    logits (see attend).
     """
     B, s_q, H, D = q.shape
     if H % num_heads_k:
@@ -162,14 +181,15 @@ def mla_decode_f64(q: np.ndarray, rows_of, cache_seqlens, num_heads_k: int, head
                 K = rows[:n, hk, :]
                 V = K[:, :head_dim_v]
                 hs = slice(hk * G, (hk + 1) * G)
-                o, l = attend(q[b, i, hs, :], K, V, softmax_scale, v_scale)
+                o, l = attend(q[b, i, hs, :], K, V, softmax_scale, v_scale,
+                              None if sinks is None else np.asarray(sinks, dtype=np.float64)[hs])
                 out[b, i, hs, :] = o
                 lse[b, hs, i] = l
     return out, lse
 
 
 def mla_decode(q_bits, kv_raw, kv_format, block_table, cache_seqlens, head_dim_v, softmax_scale,
-               causal=False, v_scale=1.0, batches=None):
+               causal=False, v_scale=1.0, batches=None, sinks=None):
     """Oracle on the raw input bytes the GPU also receives.
 
     q_bits: (B, s_q, H_q, D) uint16 bf16 bits.  kv_raw: (num_blocks, P, H_k, D)
@@ -185,4 +205,5 @@ def mla_decode(q_bits, kv_raw, kv_format, block_table, cache_seqlens, head_dim_v
         L = int(cache_seqlens[b])
         return decode_kv(gather_rows(kv_raw, block_table[b], L, P), kv_format)
 
-    return mla_decode_f64(q, rows_of, cache_seqlens, Hk, head_dim_v, softmax_scale, causal, v_scale, batches)
+    return mla_decode_f64(q, rows_of, cache_seqlens, Hk, head_dim_v, softmax_scale, causal, v_scale, batches,
+                          sinks)

@@ -315,3 +315,59 @@ def test_config1_shapes_and_pool():
     used = set(w.block_table[0, :2].tolist()) | set(w.block_table[1].tolist())
     assert len(used) == 7 and used <= set(range(8))
     assert w.q_bits.shape == (2, 1, 16, 576) and w.kv.shape == (8, 64, 1, 576)
+
+
+# ------------------------------------------------------------------ attention sinks
+# FlashInfer MLA page, ``sinks``: a per-head extra term of the softmax
+# denominator, read as a logit on the scale of softmax_scale * q.k.
+
+def _sink_workload():
+    return make_workload(seqlens=[300, 1, 0, 129], num_heads_q=8, s_q=2, seed=31)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sink_of_minus_inf_is_no_sink(causal):
+    w = _sink_workload()
+    o1, l1 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal)
+    o2, l2 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal,
+                        sinks=np.full(8, -np.inf))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sink_adds_one_denominator_term_per_head(causal):
+    """With sink logit z_h: lse' = logaddexp(lse, z_h) and out' = out * exp(lse - lse') -- the
+    no-sink result rescaled by the share of the keys in the enlarged denominator.  Distinct
+    sinks per head catch a wrong head mapping; the empty sequence (L = 0) and the causal row
+    with no key give lse' = z_h, out' = 0."""
+    w = _sink_workload()
+    sinks = np.linspace(-3.0, 4.0, 8)
+    o1, l1 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal, v_scale=0.7)
+    o2, l2 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal, v_scale=0.7,
+                        sinks=sinks)
+    z = sinks[None, :, None]                                  # lse is (B, H, s_q)
+    assert np.allclose(l2, np.logaddexp(l1, z), rtol=1e-13, atol=1e-13)
+    ratio = np.exp(l1 - l2)                                   # (B, H, s_q); 0 where l1 = -inf
+    assert np.allclose(o2, o1 * np.transpose(ratio, (0, 2, 1))[..., None], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(l2[2], np.broadcast_to(z[0], (8, 2)))     # L = 0
+    assert (o2[2] == 0).all()
+
+
+def test_sink_single_key_closed_form():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 2, D))
+    k = rng.standard_normal(D)
+    z = np.array([0.25, -1.5])
+    out, lse = mla_decode_f64(q, lambda b: k[None, None, :], [1], 1, DV, 0.5, False, v_scale=2.0, sinks=z)
+    s = 0.5 * q[0, 0] @ k
+    for h in range(2):
+        p = 1.0 / (1.0 + math.exp(z[h] - s[h]))                  # e^s / (e^s + e^z)
+        assert np.allclose(out[0, 0, h], 2.0 * p * k[:DV], rtol=1e-13)
+        assert abs(lse[0, h, 0] - math.log(math.exp(s[h]) + math.exp(z[h]))) < 1e-13
+
+
+def test_dominant_sink_silences_the_keys():
+    w = _sink_workload()
+    o, l = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, sinks=np.full(8, 200.0))
+    assert np.abs(o).max() < 1e-40
+    assert np.allclose(l, 200.0, rtol=0, atol=1e-12)
