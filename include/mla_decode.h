@@ -188,6 +188,52 @@ int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int h
                        void *workspace, size_t workspace_bytes,
                        void *out, float *lse, void *stream);
 
+/* Optional inputs of mla_decode_fwd_ext.  A zeroed struct (or a NULL ext)
+ * is plain mla_decode_fwd.  Every pointer is a device pointer or NULL.
+ *   sinks      : fp32 [num_heads_q], per-head sink logits (FlashInfer
+ *                trtllm_batch_decode_with_kv_cache_mla page, sinks: a per-head
+ *                extra term of the softmax denominator).  Read as a logit on
+ *                the scale of softmax_scale * q.k: head h's denominator gains
+ *                exp(sinks[h]), which carries no value, and lse includes it;
+ *                -inf is no sink.  Values must be finite or -inf.
+ *   bmm1_scale : fp32 [1]; when set, replaces softmax_scale (same page: the
+ *                fused bmm1/bmm2 scales may be device tensors, which then
+ *                take precedence).  Read on the device, so it is not
+ *                validated: a negative or NaN value acts as 0+.
+ *   bmm2_scale : fp32 [1]; when set, replaces v_scale.
+ *   kv_rope    : split cache (Ascend ATB MLA page, cacheMode KROPE_CTKV:
+ *                ctKV [num_blocks, block_size, kv_heads, 512] and kRope
+ *                [num_blocks, block_size, kv_heads, 64]).  When set,
+ *                kv_cache holds the 512 latent columns
+ *                [num_blocks][64][num_heads_k][512] and kv_rope the 64 rope
+ *                columns [num_blocks][64][num_heads_k][64], both of kv_dtype;
+ *                the block table indexes both.
+ *   q_rope     : split query (same page: qNope and qRope).  When set, q holds
+ *                [batch][s_q][num_heads_q][512] and q_rope the rope columns,
+ *                bf16 [batch][s_q][num_heads_q][64].
+ *   stages     : 0 or 3 = both stages; 1 = mla_decode_splits only; 2 =
+ *                mla_combine_splits only (the combine applies the sinks of
+ *                split sequences and the device bmm2_scale, so it must get the
+ *                same ext).  Other values are INVALID_ARG.
+ * head_dim stays 576 (the total width) in every layout. */
+typedef struct mla_decode_ext {
+  const float *sinks;
+  const float *bmm1_scale;
+  const float *bmm2_scale;
+  const void *kv_rope;
+  const void *q_rope;
+  int stages;
+} mla_decode_ext;
+
+/* mla_decode_fwd with the optional inputs above (NULL ext = mla_decode_fwd). */
+int mla_decode_fwd_ext(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                       const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                       const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                       int head_dim_v, float softmax_scale, float v_scale, int causal,
+                       const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                       void *workspace, size_t workspace_bytes,
+                       void *out, float *lse, void *stream, const mla_decode_ext *ext);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,8 @@ def load_library(path: Optional[str] = None):
     for fn in (lib.mla_decode_fwd, lib.mla_decode_splits, lib.mla_combine_splits):
         fn.restype = _c_int
         fn.argtypes = _DECODE_ARGTYPES
+    lib.mla_decode_fwd_ext.restype = _c_int
+    lib.mla_decode_fwd_ext.argtypes = _DECODE_ARGTYPES + [ctypes.POINTER(DecodeExt)]
     _lib = lib
     return lib
 
@@ -68,6 +70,12 @@ _DECODE_ARGTYPES = [
     _vp, _c_size,                                   # workspace, workspace_bytes
     _vp, _vp, _vp,                                  # out, lse, stream
 ]
+
+
+class DecodeExt(ctypes.Structure):
+    """mla_decode_ext of include/mla_decode.h."""
+    _fields_ = [("sinks", _vp), ("bmm1_scale", _vp), ("bmm2_scale", _vp), ("kv_rope", _vp), ("q_rope", _vp),
+                ("stages", _c_int)]
 
 
 class MlaError(RuntimeError):
@@ -178,8 +186,10 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
                    head_dim_v: int, tile_scheduler_metadata: torch.Tensor, num_splits: torch.Tensor,
                    softmax_scale: Optional[float] = None, causal: bool = False, v_scale: float = 1.0,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stage: str = "all"
-                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+                   workspace: Optional[torch.Tensor] = None, stage: str = "all",
+                   sinks: Optional[torch.Tensor] = None, bmm1_scale_tensor: Optional[torch.Tensor] = None,
+                   bmm2_scale_tensor: Optional[torch.Tensor] = None, kv_rope: Optional[torch.Tensor] = None,
+                   q_rope: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode attention (FlashMLA interface page, flash_mla_with_kvcache).
 
     q (B, s_q, H_q, 576) bf16; kv_cache (num_blocks, 64, H_k, 576) bf16 or
@@ -187,13 +197,20 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
     stage: "all" (mla_decode_fwd), or "splits" / "combine" to run one of its
     two kernels (mla_decode_splits / mla_combine_splits; pass the same out,
     lse and workspace to both).
-    softmax_scale defaults to 1/sqrt(q.shape[-1]) (for an fp8 cache pass the
-    fused bmm1 scale); v_scale is the fused bmm2 scale.  Returns
+    softmax_scale defaults to 1/sqrt(576) (for an fp8 cache pass the fused
+    bmm1 scale); v_scale is the fused bmm2 scale.  Returns
     out (B, s_q, H_q, 512) bf16 and softmax_lse (B, H_q, s_q) fp32.
+
+    Optional inputs (mla_decode_fwd_ext; FlashInfer MLA page and Ascend ATB
+    MLA page): sinks (H_q,) fp32 per-head sink logits; bmm1_scale_tensor /
+    bmm2_scale_tensor (1,) fp32 device scales replacing softmax_scale /
+    v_scale; kv_rope (num_blocks, 64, H_k, 64) with kv_cache then
+    (num_blocks, 64, H_k, 512) (split cache); q_rope (B, s_q, H_q, 64) bf16
+    with q then (B, s_q, H_q, 512) (split query).
     """
     lib = load_library()
     if softmax_scale is None:
-        softmax_scale = q.shape[-1] ** (-0.5)
+        softmax_scale = HEAD_DIM ** (-0.5)
     dev = q.device
     _need(q, "q", torch.bfloat16, dev)
     _need(kv_cache, "kv_cache", None, dev)
@@ -205,6 +222,18 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
         raise ValueError("q must be (batch, seq_len_q, num_heads_q, head_dim)")
     B, s_q, Hq, D = q.shape
     nb, page, hk, dk, code = _kv_layout(kv_cache)
+    if q_rope is not None:
+        _need(q_rope, "q_rope", torch.bfloat16, dev)
+        if D != HEAD_DIM_V or tuple(q_rope.shape) != (B, s_q, Hq, HEAD_DIM - HEAD_DIM_V):
+            raise ValueError("with q_rope, q must be (B, s_q, H_q, 512) and q_rope (B, s_q, H_q, 64)")
+        D = HEAD_DIM
+    if kv_rope is not None:
+        _need(kv_rope, "kv_rope", kv_cache.dtype, dev)
+        if dk != HEAD_DIM_V or tuple(kv_rope.shape[:-1]) != tuple(kv_cache.shape[:-1]) \
+                or kv_rope.shape[-1] != HEAD_DIM - HEAD_DIM_V:
+            raise ValueError("with kv_rope, kv_cache must end in 512 and kv_rope in 64 columns, "
+                             "with the same leading shape")
+        dk = HEAD_DIM
     if dk != D:
         raise ValueError("q and kv_cache head_dim differ")
     if block_table.dim() != 2 or block_table.shape[0] != B:
@@ -236,13 +265,29 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, dev)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, dev)
+        if tuple(sinks.shape) != (Hq,):
+            raise ValueError("sinks must be (num_heads_q,)")
+    for t, name in ((bmm1_scale_tensor, "bmm1_scale_tensor"), (bmm2_scale_tensor, "bmm2_scale_tensor")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if t.numel() != 1:
+                raise ValueError(f"{name} must hold one value")
+    stages = {"all": 3, "splits": 1, "combine": 2}[stage]
+    args = (_ptr(q), B, s_q, Hq, D, _ptr(kv_cache), code, nb, page, hk,
+            _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+            head_dim_v, float(softmax_scale), float(v_scale), int(bool(causal)),
+            _ptr(tile_scheduler_metadata), num_parts, _ptr(num_splits),
+            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev))
     with torch.cuda.device(dev):
-        fn = {"all": lib.mla_decode_fwd, "splits": lib.mla_decode_splits, "combine": lib.mla_combine_splits}[stage]
-        rc = fn(_ptr(q), B, s_q, Hq, D, _ptr(kv_cache), code, nb, page, hk,
-                                _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
-                                head_dim_v, float(softmax_scale), float(v_scale), int(bool(causal)),
-                                _ptr(tile_scheduler_metadata), num_parts, _ptr(num_splits),
-                                _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev))
+        if any(t is not None for t in (sinks, bmm1_scale_tensor, bmm2_scale_tensor, kv_rope, q_rope)):
+            ext = DecodeExt(_ptr(sinks), _ptr(bmm1_scale_tensor), _ptr(bmm2_scale_tensor), _ptr(kv_rope),
+                            _ptr(q_rope), stages)
+            rc = lib.mla_decode_fwd_ext(*args, ctypes.byref(ext))
+        else:
+            fn = {3: lib.mla_decode_fwd, 1: lib.mla_decode_splits, 2: lib.mla_combine_splits}[stages]
+            rc = fn(*args)
     _check(rc)
     return out, lse
 

@@ -145,7 +145,7 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
                    int head_dim_v, float softmax_scale, float v_scale, int causal,
                    const int32_t *tile_md, int num_parts, const int32_t *num_splits,
                    void *workspace, size_t workspace_bytes,
-                   void *out, float *lse, void *stream) {
+                   void *out, float *lse, void *stream, const mla_decode_ext *ext = nullptr) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !tile_md || !num_splits || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, block_table, cache_seqlens, tile_md, num_splits, out and lse must be non-NULL");
   if (batch < 1 || s_q < 1 || num_heads_q < 1 || num_heads_k < 1 || num_blocks < 1 || max_blocks_per_seq < 1 ||
@@ -202,6 +202,20 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   a.causal = causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
+  a.q_stride = head_dim;
+  a.q_rope = nullptr;
+  a.kv_rope = nullptr;
+  a.sinks = nullptr;
+  a.bmm1_dev = nullptr;
+  a.bmm2_dev = nullptr;
+  if (ext) {
+    a.q_rope = (const uint16_t *)ext->q_rope;
+    a.q_stride = ext->q_rope ? MLA_HEAD_DIM_V : MLA_HEAD_DIM;
+    a.kv_rope = (const uint8_t *)ext->kv_rope;
+    a.sinks = ext->sinks;
+    a.bmm1_dev = ext->bmm1_scale;
+    a.bmm2_dev = ext->bmm2_scale;
+  }
   if (stage & 1) {
     hipError_t e = mla::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, hipGetErrorString(e));
@@ -251,6 +265,23 @@ int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int h
   return decode_call(2, q, batch, s_q, num_heads_q, head_dim, kv_cache, kv_dtype, num_blocks, page_block_size,
                      num_heads_k, block_table, max_blocks_per_seq, cache_seqlens, head_dim_v, softmax_scale, v_scale,
                      causal, tile_md, num_parts, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int mla_decode_fwd_ext(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                       const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                       const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                       int head_dim_v, float softmax_scale, float v_scale, int causal,
+                       const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                       void *workspace, size_t workspace_bytes,
+                       void *out, float *lse, void *stream, const mla_decode_ext *ext) {
+  int stage = 3;
+  if (ext) {
+    if (ext->stages < 0 || ext->stages > 3) return fail(MLA_ERR_INVALID_ARG, "ext->stages must be 0, 1, 2 or 3");
+    if (ext->stages) stage = ext->stages;
+  }
+  return decode_call(stage, q, batch, s_q, num_heads_q, head_dim, kv_cache, kv_dtype, num_blocks, page_block_size,
+                     num_heads_k, block_table, max_blocks_per_seq, cache_seqlens, head_dim_v, softmax_scale, v_scale,
+                     causal, tile_md, num_parts, num_splits, workspace, workspace_bytes, out, lse, stream, ext);
 }
 
 }  // extern "C"

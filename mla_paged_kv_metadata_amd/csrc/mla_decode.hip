@@ -112,27 +112,41 @@ __device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) 
 // addresses (k even / odd) plus the immediate 128 * (k / 2).  The whole page
 // is copied; rows past the sequence end are zeroed in LDS afterwards
 // (zero_tail_rows) before any wave reads them.
+//
+// Split cache (kSplit; Ascend ATB MLA page, cacheMode KROPE_CTKV: ctKV
+// [num_blocks, block_size, kv_heads, 512] and kRope [.., 64] as two tensors):
+// the eight latent groups come from the ctKV rows and group 8 (the 64 rope
+// columns) from the kRope rows, into the same LDS image.
 struct PageSrc {
-  const uint8_t *even, *odd;   // this lane's source for token blocks 2w, 2w + 1 (group 0)
+  const uint8_t *even, *odd;             // this lane's source for token blocks 2w, 2w + 1 (group 0)
+  const uint8_t *rope_even, *rope_odd;   // split cache: the same tokens' rope columns
 };
-__device__ __forceinline__ PageSrc page_src_bf16(const uint8_t *tok0, int tok_stride, int wave, int lane) {
+template <bool kSplit>
+__device__ __forceinline__ PageSrc page_src_bf16(const uint8_t *tok0, const uint8_t *rope0, int tok_stride,
+                                                 int rope_stride, int wave, int lane) {
   const int lt = lane >> 3;
   // token t = 16w + 8*(k&1) + lt: h(t) = (lt1, lt2, k&1) -> chunk (lane & 7) ^ h(t)
   PageSrc p;
   p.even = tok0 + (16 * wave + lt) * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;
   p.odd = tok0 + (16 * wave + 8 + lt) * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
+  p.rope_even = p.rope_odd = nullptr;
+  if (kSplit) {
+    p.rope_even = rope0 + (16 * wave + lt) * rope_stride + ((lane & 7) ^ swz_h(lt)) * 16;
+    p.rope_odd = rope0 + (16 * wave + 8 + lt) * rope_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
+  }
   return p;
 }
-template <int k>
+template <bool kSplit, int k>
 __device__ __forceinline__ void dma_bf16_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
   const int I = 8 * (k >> 1) + 2 * wave + (k & 1);
-  lds_dma16<128 * (k >> 1)>((k & 1) ? p.odd : p.even, dst + I * 1024);
+  if constexpr (kSplit && (k >> 1) == 8) lds_dma16<0>((k & 1) ? p.rope_odd : p.rope_even, dst + I * 1024);
+  else lds_dma16<128 * (k >> 1)>((k & 1) ? p.odd : p.even, dst + I * 1024);
 }
-template <int k = 0>
+template <bool kSplit, int k = 0>
 __device__ __forceinline__ void dma_page_bf16(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
   if constexpr (k < kPageLoads) {
-    dma_bf16_step<k>(p, dst, wave);
-    dma_page_bf16<k + 1>(p, dst, wave);
+    dma_bf16_step<kSplit, k>(p, dst, wave);
+    dma_page_bf16<kSplit, k + 1>(p, dst, wave);
   }
 }
 
@@ -148,30 +162,36 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid,
 
 // HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: slot
 // I = 4 * (column group of 64 B) + token block (16 tokens); wave w copies
-// token block w, instruction k covering column group k.
-__device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *tok0, int tok_stride, int wave, int lane) {
+// token block w, instruction k covering column group k (group 8, the rope
+// columns, from the kRope rows of a split cache).
+template <bool kSplit>
+__device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *tok0, const uint8_t *rope0, int tok_stride,
+                                                int rope_stride, int wave, int lane) {
   PageSrc p;
   p.even = p.odd = tok0 + (16 * wave + (lane >> 2)) * tok_stride + (lane & 3) * 16;
+  p.rope_even = p.rope_odd = kSplit ? rope0 + (16 * wave + (lane >> 2)) * rope_stride + (lane & 3) * 16 : nullptr;
   return p;
 }
-template <int k>
+template <bool kSplit, int k>
 __device__ __forceinline__ void dma_fp8_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
-  lds_dma16<64 * k>(p.even, dst + (4 * k + wave) * 1024);
+  if constexpr (kSplit && k == 8) lds_dma16<0>(p.rope_even, dst + (4 * k + wave) * 1024);
+  else lds_dma16<64 * k>(p.even, dst + (4 * k + wave) * 1024);
 }
-template <int k = 0>
+template <bool kSplit, int k = 0>
 __device__ __forceinline__ void dma_page_fp8(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
   if constexpr (k < kF8PageLoads) {
-    dma_fp8_step<k>(p, dst, wave);
-    dma_page_fp8<k + 1>(p, dst, wave);
+    dma_fp8_step<kSplit, k>(p, dst, wave);
+    dma_page_fp8<kSplit, k + 1>(p, dst, wave);
   }
 }
 
 // Instruction k of a page copy for a k known only after loop unrolling (the
 // switch folds away once k is a constant).
+template <bool kSplit>
 __device__ __forceinline__ void dma_bf16_dispatch(const PageSrc &p, LDS_AS uint8_t *dst, int wave, int k) {
   switch (k) {
 #define MLA_DMA_CASE(n) \
-  case n: dma_bf16_step<n>(p, dst, wave); break;
+  case n: dma_bf16_step<kSplit, n>(p, dst, wave); break;
     MLA_DMA_CASE(0) MLA_DMA_CASE(1) MLA_DMA_CASE(2) MLA_DMA_CASE(3) MLA_DMA_CASE(4) MLA_DMA_CASE(5)
     MLA_DMA_CASE(6) MLA_DMA_CASE(7) MLA_DMA_CASE(8) MLA_DMA_CASE(9) MLA_DMA_CASE(10) MLA_DMA_CASE(11)
     MLA_DMA_CASE(12) MLA_DMA_CASE(13) MLA_DMA_CASE(14) MLA_DMA_CASE(15) MLA_DMA_CASE(16) MLA_DMA_CASE(17)
@@ -179,10 +199,11 @@ __device__ __forceinline__ void dma_bf16_dispatch(const PageSrc &p, LDS_AS uint8
     default: break;
   }
 }
+template <bool kSplit>
 __device__ __forceinline__ void dma_fp8_dispatch(const PageSrc &p, LDS_AS uint8_t *dst, int wave, int k) {
   switch (k) {
 #define MLA_DMA_CASE(n) \
-  case n: dma_fp8_step<n>(p, dst, wave); break;
+  case n: dma_fp8_step<kSplit, n>(p, dst, wave); break;
     MLA_DMA_CASE(0) MLA_DMA_CASE(1) MLA_DMA_CASE(2) MLA_DMA_CASE(3) MLA_DMA_CASE(4) MLA_DMA_CASE(5)
     MLA_DMA_CASE(6) MLA_DMA_CASE(7) MLA_DMA_CASE(8)
 #undef MLA_DMA_CASE
@@ -289,7 +310,7 @@ struct NextPage {
 // Returns true (wave-uniform) when some row of this wave needs a re-run.
 //   scale_log2 > 0 (softmax_scale * log2 e, clamped away from 0 by the caller);
 //   mask: some key of this page may be invisible to some row of the wave.
-template <bool kFp8>
+template <bool kFp8, bool kSplit>
 __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
                                             f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
                                             int lane, int key0, int nvis, float scale_log2, bool mask,
@@ -407,8 +428,8 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
     else mfma_qk(sc, kf[sl], qf[ks]);
     if (g + kPre < 2 * kKSteps) kf[sl] = kload((g + kPre) % kKSteps, (g + kPre) / kKSteps);
     if (nx.valid && g % kDmaEvery == 0) {
-      if (kFp8) dma_fp8_dispatch(nx.src, nx.dst, nx.wave, g / kDmaEvery);
-      else dma_bf16_dispatch(nx.src, nx.dst, nx.wave, g / kDmaEvery);
+      if (kFp8) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
+      else dma_bf16_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
     }
   };
 #pragma unroll
@@ -576,7 +597,7 @@ __device__ __forceinline__ int xcd_part(int w, int n) {
   return x * q + min(x, r) + i;
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
@@ -605,14 +626,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int wrow0 = rt * kRowsPerTile + wave * 32;
   const bool active = wrow0 < a.rows;                 // wave-uniform
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
-  const float scale_log2 = fmaxf(a.scale_log2, 1e-30f);
+  // A device-held bmm1 scale replaces the host value (FlashInfer MLA page:
+  // bmm1_scale / bmm2_scale may be device tensors); negative or NaN values
+  // act as 0+.
+  const float scale_log2 = fmaxf(a.bmm1_dev ? *a.bmm1_dev * kLog2e : a.scale_log2, 1e-30f);
 
   const int elem = kFp8 ? 1 : 2;
-  const int tok_stride = a.hk * kHeadDim * elem;
+  constexpr int kRowDim = kSplit ? kHeadDimV : kHeadDim;   // columns of a kv_cache row
+  const int tok_stride = a.hk * kRowDim * elem;
   const long page_stride = (long)kPage * tok_stride;
-  const uint8_t *kv_head = a.kv + (long)hk * kHeadDim * elem;
-  auto page_addr = [&](int pg) -> const uint8_t * {
-    return kv_head + (long)max(0, min(pg, a.num_blocks - 1)) * page_stride;
+  const uint8_t *kv_head = a.kv + (long)hk * kRowDim * elem;
+  const int rope_stride = a.hk * (kHeadDim - kHeadDimV) * elem;
+  const uint8_t *rope_head = kSplit ? a.kv_rope + (long)hk * (kHeadDim - kHeadDimV) * elem : nullptr;
+  // This lane's copy sources for page pg (index clamped into the pool).
+  auto src_of = [&](int pg) -> PageSrc {
+    const long pc = max(0, min(pg, a.num_blocks - 1));
+    const uint8_t *t0 = kv_head + pc * page_stride;
+    const uint8_t *r0 = kSplit ? rope_head + pc * kPage * rope_stride : nullptr;
+    return kFp8 ? page_src_fp8<kSplit>(t0, r0, tok_stride, rope_stride, wave, lane)
+                : page_src_bf16<kSplit>(t0, r0, tok_stride, rope_stride, wave, lane);
   };
   // Lengths and page ranges are clamped so that every global address stays
   // inside its buffer whatever the table or cache_seqlens hold.
@@ -621,14 +653,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
   bf16x8 qf[kKSteps];
   // This lane's q fragments: row (qi, h) of sequence b, dims 16 ks + 8 hl .. +7.
-  auto q_row = [&](int b) -> const uint16_t * {
-    const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
-    return a.q + (((long)min(b, a.batch - 1) * a.s_q + c.qi) * a.hq + c.h) * kHeadDim + 8 * (lane_id_here() >> 5);
-  };
+  // The rope columns (k-steps 32..35) come from q_rope when q is split
+  // (Ascend ATB MLA page: qNope [.., 512] and qRope [.., 64]).
   auto load_q = [&](int b) {
-    const uint16_t *qrow = q_row(b);
+    const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
+    const long r = ((long)min(b, a.batch - 1) * a.s_q + c.qi) * a.hq + c.h;
+    const int hl8 = 8 * (lane_id_here() >> 5);
+    const uint16_t *qn = a.q + r * a.q_stride + hl8;
+    const uint16_t *qr = a.q_rope ? a.q_rope + r * (kHeadDim - kHeadDimV) + hl8 : qn + kHeadDimV;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qf[ks] = *(const bf16x8 *)(ks < kHeadDimV / 16 ? qn + 16 * ks : qr + 16 * (ks - kHeadDimV / 16));
   };
 
   int cur = 0;              // buffer that receives / holds the next page to process
@@ -649,9 +684,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int nblk0 = (len0 + kPage - 1) / kPage;
     const int hi0 = seq_end(b0, nblk0);
     if (hi0 > first0) {                               // then the split's first page is first0
-      const uint8_t *src = page_addr(__builtin_amdgcn_readfirstlane(bt_pref));
-      if (kFp8) dma_page_fp8(page_src_fp8(src, tok_stride, wave, lane), stages[0], wave);
-      else dma_page_bf16(page_src_bf16(src, tok_stride, wave, lane), bufs[0], wave);
+      const PageSrc src = src_of(__builtin_amdgcn_readfirstlane(bt_pref));
+      if (kFp8) dma_page_fp8<kSplit>(src, stages[0], wave);
+      else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
     }
   }
@@ -670,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int32_t *bt = a.block_table + (long)b * a.max_blocks;
     // First page of the next split of this part (page 0 of b + 1), copied
     // while the last page of this split is processed.
-    const uint8_t *next_src = kv_head;
+    int next_pg = 0;
     bool next_has_pages = false;
     const int bt_this = bt_pref;                          // block-table lanes of this split (loaded earlier)
     if (b < b1) {
@@ -679,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       next_has_pages = seq_end(b + 1, nblk_n) > 0;
       if (next_has_pages) {
         const int32_t *bt_n = a.block_table + (long)(b + 1) * a.max_blocks;
-        next_src = page_addr(bt_n[0]);
+        next_pg = bt_n[0];
         bt_pref = bt_n[min(lane, nblk_n - 1)];            // next split starts at page 0
       }
     }
@@ -707,8 +742,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       for (int pass = 0;; ++pass) {
         bool need = false;
         if (!have_first) {
-          if (kFp8) dma_page_fp8(page_src_fp8(page_addr(page_of(lo)), tok_stride, wave, lane), stages[cur], wave);
-          else dma_page_bf16(page_src_bf16(page_addr(page_of(lo)), tok_stride, wave, lane), bufs[cur], wave);
+          if (kFp8) dma_page_fp8<kSplit>(src_of(page_of(lo)), stages[cur], wave);
+          else dma_page_bf16<kSplit>(src_of(page_of(lo)), bufs[cur], wave);
         }
         have_first = false;
         for (int j = lo; j < hi; ++j) {
@@ -723,8 +758,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           }
           NextPage nx;
           nx.valid = j + 1 < hi || next_has_pages;
-          const uint8_t *ntok0 = j + 1 < hi ? page_addr(page_of(j + 1)) : next_src;
-          nx.src = kFp8 ? page_src_fp8(ntok0, tok_stride, wave, lane) : page_src_bf16(ntok0, tok_stride, wave, lane);
+          nx.src = src_of(j + 1 < hi ? page_of(j + 1) : next_pg);
           nx.dst = kFp8 ? stages[cur ^ 1] : bufs[cur ^ 1];
           nx.wave = wave;
           const LDS_AS uint8_t *pg;
@@ -736,11 +770,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
             pg = bufs[cur];
           }
           if (active) {
-            need |= attend_page<kFp8>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
+            need |= attend_page<kFp8, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
                                       (j + 1) * kPage > nvis_min, nx);
           } else if (nx.valid) {                    // a wave without rows still copies its share
-            if (kFp8) dma_page_fp8(nx.src, nx.dst, wave);
-            else dma_page_bf16(nx.src, nx.dst, wave);
+            if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
+            else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
           }
           cur ^= 1;
         }
@@ -771,15 +805,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     // past the barriers above; fp8: the bf16 page), never through bufs[cur],
     // which may be receiving the next split's first page.
     if (active) {
-      const bool has = l > 0.f;
-      const float inv = has ? 1.f / l : 0.f;
-      const float lse_v = has ? (m + __log2f(l)) * kLn2 : kNegInf;
       const bool direct = nsplit <= 1;
       const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
+      // Normaliser.  With a sink logit z (FlashInfer MLA page, sinks; a
+      // sequence with one split takes it here, split sequences in the
+      // combine) the denominator l 2^m gains e^z = 2^zs: with M = max(m, zs)
+      // it is lt 2^M, lt = l 2^(m-M) + 2^(zs-M), and O (relative to 2^m) is
+      // scaled by 2^(m-M) / lt.  Without a sink this is 1/l and m + log2 l.
+      float zs = kNegInf;
+      if (direct && a.sinks) zs = a.sinks[c.h] * kLog2e;
+      const float mm = fmaxf(m, zs);
+      float lt = 0.f, inv = 0.f;
+      if (mm != kNegInf) {
+        const float am = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+        lt = l * am + __builtin_amdgcn_exp2f(zs - mm);
+        inv = am / lt;
+      }
+      const float lse_v = lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * kStageWave;
-      store_rows(o, direct ? inv * a.v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow,
+      const float v_scale = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
+      store_rows(o, direct ? inv * v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow,
                  max(0, min(32, uniform_here(a.rows) - wrow0)),
                  stage);
       if (lane_id_here() < 32 && c.row < a.rows) {
@@ -811,7 +858,18 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
   const long sstride = (long)a.hk * a.rows;
   const float *pl = a.part_lse + ((long)slot0 * a.hk + hk) * a.rows + row;
   const uint16_t *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
+  const int qi = row / a.group;
+  const int h = hk * a.group + (row - qi * a.group);
+  // A sink logit z joins as one more term of weight e^z and no value
+  // (FlashInfer MLA page, sinks): the running state starts at mu = z, Z = 1.
   float mu = kNegInf, Z = 0.f;
+  if (a.sinks) {
+    const float z = a.sinks[h];
+    if (z > kNegInf) {
+      mu = z;
+      Z = 1.f;
+    }
+  }
   float acc[8] = {};
   for (int k0 = 0; k0 < n; k0 += kCombineBatch) {
     float lk[kCombineBatch];
@@ -840,9 +898,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
       for (int e = 0; e < 8; ++e) acc[e] += w * (float)vk[i][e];
     }
   }
-  const float inv = Z > 0.f ? a.v_scale / Z : 0.f;
-  const int qi = row / a.group;
-  const int h = hk * a.group + (row - qi * a.group);
+  const float inv = Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
   uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + lane * 8;
   bf16x8 ov;
 #pragma unroll
@@ -857,18 +913,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const size_t smem = 2 * (size_t)kPageBytes + 16;   // pages (or page + fp8 staging) + restart flag
   static_assert(kPageBytes + 2 * kF8PageBytes == 2 * kPageBytes, "fp8 staging fills the second page slot");
   const dim3 grid(a.num_parts, a.row_tiles * a.hk);   // one persistent workgroup per part
-  if (a.kv_fp8) {
-    hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  auto launch = [&](auto kernel) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(kThreads), smem, stream, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void *)mla_decode_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(kThreads), smem, stream, a);
-  }
-  return hipGetLastError();
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), smem, stream, a);
+    return hipGetLastError();
+  };
+  if (a.kv_fp8) return a.kv_rope ? launch(mla_decode_kernel<true, true>) : launch(mla_decode_kernel<true, false>);
+  return a.kv_rope ? launch(mla_decode_kernel<false, true>) : launch(mla_decode_kernel<false, false>);
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {

@@ -13,8 +13,8 @@ constexpr int kRowsPerTile = 128;     // rows (query heads x s_q) per decode wor
 constexpr int kMetaThreads = 1024;
 
 struct DecodeArgs {
-  const uint16_t *q;          // bf16 bits [B][s_q][Hq][576]
-  const uint8_t *kv;          // [num_blocks][64][Hk][576] bf16 or e4m3fn
+  const uint16_t *q;          // bf16 bits [B][s_q][Hq][q_stride]
+  const uint8_t *kv;          // [num_blocks][64][Hk][576 or 512] bf16 or e4m3fn
   const int32_t *block_table; // [B][max_blocks]
   const int32_t *seqlens;     // [B]
   const int32_t *tile_md;     // [num_parts][8], one row per part
@@ -27,6 +27,13 @@ struct DecodeArgs {
   int kv_fp8, causal;
   float scale_log2;           // softmax_scale * log2(e)
   float v_scale;
+  int q_stride;               // elements per q row: 576, or 512 with q_rope
+  const uint16_t *q_rope;     // nullptr, or bf16 bits [B][s_q][Hq][64]: the rope columns of q
+  const uint8_t *kv_rope;     // nullptr, or [num_blocks][64][Hk][64]: the rope columns of the cache
+                              // (kv then holds [num_blocks][64][Hk][512])
+  const float *sinks;         // nullptr, or fp32 [Hq] per-head sink logits
+  const float *bmm1_dev;      // nullptr, or fp32 [1] replacing softmax_scale
+  const float *bmm2_dev;      // nullptr, or fp32 [1] replacing v_scale
 };
 
 hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int fixed_cost,

@@ -97,3 +97,50 @@ def test_no_device_is_reported_when_arguments_are_valid():
     assert _decode(lib) == 4
     n = ctypes.c_int(0)
     assert lib.mla_num_parts(4, 128, 1, ctypes.byref(n)) == 4
+
+
+def _decode_ext(lib, ext, **kw):
+    a = dict(q=1, batch=2, s_q=1, hq=16, d=576, kv=1, dt=0, nb=8, page=64, hk=1, bt=1, maxb=5, sl=1, dv=512,
+             scale=1 / 24, vs=1.0, causal=0, md=1, parts=4, ns=1, ws=1, wsb=1 << 30, out=1, lse=1, stream=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.mla_decode_fwd_ext(P(a["q"]), a["batch"], a["s_q"], a["hq"], a["d"], P(a["kv"]), a["dt"], a["nb"],
+                                  a["page"], a["hk"], P(a["bt"]), a["maxb"], P(a["sl"]), a["dv"], a["scale"],
+                                  a["vs"], a["causal"], P(a["md"]), a["parts"], P(a["ns"]), P(a["ws"]), a["wsb"],
+                                  P(a["out"]), P(a["lse"]), P(a["stream"]),
+                                  None if ext is None else ctypes.byref(ext))
+
+
+def test_header_declares_the_ext_struct_with_the_binding_layout():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct mla_decode_ext \{(.*?)\} mla_decode_ext;", src, flags=re.S).group(1)
+    fields = re.findall(r"\b(\w+);", body)
+    assert fields == [f for f, _ in mla.DecodeExt._fields_]
+
+
+@pytest.mark.parametrize("stages,status", [(-1, 1), (4, 1)])
+def test_ext_rejects_bad_stages_before_any_device_call(stages, status):
+    ext = mla.DecodeExt(None, None, None, None, None, stages)
+    assert _decode_ext(mla.load_library(), ext) == status
+
+
+def test_ext_applies_the_plain_checks():
+    lib = mla.load_library()
+    ext = mla.DecodeExt(None, None, None, None, None, 0)
+    assert _decode_ext(lib, ext, q=0) == 1
+    assert _decode_ext(lib, None, scale=-1.0) == 2
+    assert _decode_ext(lib, ext, wsb=16) == 3
+
+
+def test_python_wrapper_checks_split_layout_shapes():
+    import torch
+    q = torch.zeros((1, 1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 64, 1, 512), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    sl = torch.zeros((1,), dtype=torch.int32)
+    md = torch.zeros((4, 8), dtype=torch.int32)
+    ns = torch.zeros((2,), dtype=torch.int32)
+    with pytest.raises(ValueError):      # kv_rope of the wrong width
+        mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, kv_rope=torch.zeros((2, 64, 1, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):      # q_rope with a 576-wide q
+        mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, q_rope=torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16))
