@@ -214,6 +214,10 @@ def main():
     ap.add_argument("--num-parts", type=int, default=None, help="override the scheduler's balancing target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (mla_decode_fwd_ext)")
+    ap.add_argument("--split-cache", action="store_true",
+                    help="latent/rope cache and q as separate tensors (mla_decode_fwd_ext)")
+    ap.add_argument("--device-scales", action="store_true", help="bmm1/bmm2 scales held on the device")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -268,6 +272,26 @@ def main():
     else:
         kv_host = torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16)
     kvs = [kv_host.to(dev) for _ in range(max(1, args.copies))]
+    # Optional inputs of mla_decode_fwd_ext: per-head sinks, the split
+    # latent/rope cache (with split q), device-held scales.
+    ext = {}
+    sinks_np = None
+    if args.sinks:
+        sinks_np = np.linspace(-1.0, 3.0, w.num_heads_q).astype(np.float32)
+        ext["sinks"] = torch.from_numpy(sinks_np).to(dev)
+    if args.device_scales:
+        ext["bmm1_scale_tensor"] = torch.tensor([s1], dtype=torch.float32, device=dev)
+        ext["bmm2_scale_tensor"] = torch.tensor([s2], dtype=torch.float32, device=dev)
+    ropes = [None] * len(kvs)
+    if args.split_cache:
+        ropes = [kv[..., 512:].contiguous() for kv in kvs]
+        kvs = [kv[..., :512].contiguous() for kv in kvs]
+        ext["q_rope"] = q[..., 512:].contiguous()
+        q = q[..., :512].contiguous()
+        torch.cuda.empty_cache()
+
+    def ext_for(i):
+        return dict(ext, kv_rope=ropes[i % len(kvs)]) if args.split_cache else ext
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.cache_seqlens).to(dev)
     hpk = w.heads_per_head_k
@@ -285,9 +309,9 @@ def main():
         kv = kvs[i % len(kvs)]
         mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, tile_md=md, num_splits=ns)
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
-                           lse=lse, workspace=ws, stage="splits")
+                           lse=lse, workspace=ws, stage="splits", **ext_for(i))
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
-                           lse=lse, workspace=ws, stage="combine")
+                           lse=lse, workspace=ws, stage="combine", **ext_for(i))
 
     for i in range(2):                      # first launches (library and allocator set-up)
         step(i)
@@ -341,11 +365,11 @@ def main():
 
     def decode_call(i):
         mla.mla_decode_fwd(q, kvs[i % len(kvs)], bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2,
-                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="splits")
+                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="splits", **ext_for(i))
 
     def combine_call(i):
         mla.mla_decode_fwd(q, kvs[i % len(kvs)], bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2,
-                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="combine")
+                           causal=w.causal, out=out, lse=lse, workspace=ws, stage="combine", **ext_for(i))
 
     def kernel_us(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -389,7 +413,7 @@ def main():
         from oracle import mla_decode as oracle_decode
         bs = [0, w.batch // 4, w.batch - 1]
         ro, rl = oracle_decode(w.q_bits, w.kv, w.kv_dtype, w.block_table, w.cache_seqlens, 512, s1, w.causal, s2,
-                               batches=bs)
+                               batches=bs, sinks=None if sinks_np is None else sinks_np.astype(np.float64))
         o = out.float().cpu().numpy()[bs]
         l = lse.cpu().numpy()[bs]
         coef = 5e-2 if fp8 else 1e-2
@@ -411,7 +435,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": measured_traffic() if args.config == 2 else None,
+    plain = not (args.sinks or args.split_cache or args.device_scales)
+    roof.update({"traffic": measured_traffic() if args.config == 2 and plain else None,
                  "kernel": f"mla_decode_kernel<{'fp8' if fp8 else 'bf16'}>", "alg_bytes_per_launch": alg_bytes,
                  "alg_flops_per_launch": flops, "kernel_tflops": round(dec_tflops, 1),
                  "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)})
@@ -437,7 +462,9 @@ def main():
                                                     "bf16 q ~N(0,1), default scale",
                    "batch": w.batch, "seq_len_q": w.s_q, "num_heads_q": w.num_heads_q, "causal": bool(w.causal),
                    "kv_dtype": w.kv_dtype, "total_keys": int(w.cache_seqlens.sum()), "num_parts": P,
-                   "kv_copies": len(kvs)},
+                   "kv_copies": len(kvs),
+                   "inputs": "+".join(n for n, f in (("sinks", args.sinks), ("split_cache_q", args.split_cache),
+                                                     ("device_scales", args.device_scales)) if f) or "plain"},
         "timing": timing,
         "kv_gbps_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_gbps_decode": round(kv_bytes / dec_s / 1e9, 1),

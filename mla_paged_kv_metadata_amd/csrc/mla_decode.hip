@@ -837,52 +837,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   }
 }
 
-// Merge the split partials of every sequence with more than one split:
-// out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
-// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  One wave per
-// row, 8 dims per lane; the splits are read 8 at a time (all loads of a batch
-// in flight together) with the running max rescaling the sums between
-// batches.
-constexpr int kCombineBatch = 8;
-__global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
-  const int b = blockIdx.x;
-  const int nrows = a.batch + a.num_parts - 1;        // partial slots written by the decode kernel
-  const int slot0 = max(0, min(a.num_splits[b], nrows));
-  const int n = min(a.num_splits[b + 1] - slot0, nrows - slot0);
-  if (n <= 1) return;
-  const int groups = (a.rows + 3) / 4;
-  const int hk = blockIdx.y / groups;
-  const int row = (blockIdx.y - hk * groups) * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const int lane = threadIdx.x & 63;
-  const long sstride = (long)a.hk * a.rows;
-  const float *pl = a.part_lse + ((long)slot0 * a.hk + hk) * a.rows + row;
-  const uint16_t *po = a.part_o + (((long)slot0 * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
-  const int qi = row / a.group;
-  const int h = hk * a.group + (row - qi * a.group);
-  // A sink logit z joins as one more term of weight e^z and no value
-  // (FlashInfer MLA page, sinks): the running state starts at mu = z, Z = 1.
-  float mu = kNegInf, Z = 0.f;
-  if (a.sinks) {
-    const float z = a.sinks[h];
-    if (z > kNegInf) {
-      mu = z;
-      Z = 1.f;
-    }
-  }
-  float acc[8] = {};
-  for (int k0 = 0; k0 < n; k0 += kCombineBatch) {
-    float lk[kCombineBatch];
-    bf16x8 vk[kCombineBatch];
+// Running merge of splits 0..n-1 (kBatch per iteration, all their loads in
+// flight together; the running max rescales the sums) of one row into
+// (mu, Z, acc): sum_k e^(lse_k - mu) = Z and sum_k e^(lse_k - mu) O_k = acc.
+template <int kBatch>
+__device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po, long sstride, int n, float &mu,
+                                             float &Z, float (&acc)[8]) {
+  for (int k0 = 0; k0 < n; k0 += kBatch) {
+    float lk[kBatch];
+    bf16x8 vk[kBatch];
 #pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i) {
+    for (int i = 0; i < kBatch; ++i) {
       const int k = min(k0 + i, n - 1);               // past n: a repeat, weighted 0 below
       lk[i] = pl[k * sstride];
       vk[i] = *(const bf16x8 *)(po + k * sstride * kHeadDimV);
     }
     float mb = mu;
 #pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i)
+    for (int i = 0; i < kBatch; ++i)
       if (k0 + i < n) mb = fmaxf(mb, lk[i]);
     if (mb == kNegInf) continue;                      // every split so far is empty
     const float sc = __builtin_amdgcn_exp2f((mu - mb) * kLog2e);   // 0 while mu = -inf
@@ -891,12 +863,101 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeArgs a) {
     for (int e = 0; e < 8; ++e) acc[e] *= sc;
     mu = mb;
 #pragma unroll
-    for (int i = 0; i < kCombineBatch; ++i) {
+    for (int i = 0; i < kBatch; ++i) {
       const float w = k0 + i < n ? __builtin_amdgcn_exp2f((lk[i] - mu) * kLog2e) : 0.f;
       Z += w;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += w * (float)vk[i][e];
     }
+  }
+}
+
+// Folds the state (mu2, Z2, acc2) into (mu, Z, acc) (both relative to their
+// own max; a state with mu = -inf is empty).
+__device__ __forceinline__ void fold_state(float &mu, float &Z, float (&acc)[8], float mu2, float Z2,
+                                           const float (&acc2)[8]) {
+  const float mm = fmaxf(mu, mu2);
+  if (mm == kNegInf) return;
+  const float s1 = mu == kNegInf ? 0.f : __builtin_amdgcn_exp2f((mu - mm) * kLog2e);
+  const float s2 = mu2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((mu2 - mm) * kLog2e);
+  Z = Z * s1 + Z2 * s2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = acc[e] * s1 + acc2[e] * s2;
+  mu = mm;
+}
+
+// Merge the split partials of every sequence with more than one split:
+// out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
+// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  8 dims per
+// lane, workgroups of 4 waves.  Two launch shapes, chosen on the host:
+//   - 4 rows per workgroup, one wave per row (batches with a few splits per
+//     sequence);
+//   - when there are more than 4 parts per sequence, so that some sequence
+//     may be split many ways: one workgroup per (sequence, row).  A sequence
+//     with at most kCombineWide splits is merged by the first wave alone (the
+//     others exit at once); one with more spreads each row over the 4 waves --
+//     wave q merges splits q, q + 4, ... and the first wave folds the four
+//     states from LDS -- so a row spread over hundreds of parts gets four
+//     waves' worth of loads in flight.  A sink logit z (FlashInfer
+// MLA page, sinks) is folded last as a state (z, 1, 0): one more term of
+// weight e^z and no value.
+constexpr int kCombineWays = 4;
+constexpr int kCombineWide = 8;
+__host__ __device__ inline bool combine_per_row(const DecodeArgs &a) { return a.num_parts > 4 * a.batch; }
+__global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const DecodeArgs a) {
+  __shared__ float st_mu[kCombineWays], st_z[kCombineWays];
+  __shared__ __attribute__((aligned(16))) float st_acc[kCombineWays][64 * 8];
+  const int b = blockIdx.y;
+  const int nrows = a.batch + a.num_parts - 1;        // partial slots written by the decode kernel
+  const int slot0 = max(0, min(a.num_splits[b], nrows));
+  const int n = min(a.num_splits[b + 1] - slot0, nrows - slot0);
+  if (n <= 1) return;                                 // workgroup-uniform
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int hk, row;
+  bool wide = false;                                  // workgroup-uniform
+  if (combine_per_row(a)) {
+    hk = blockIdx.x / a.rows;
+    row = blockIdx.x - hk * a.rows;
+    wide = n > kCombineWide;
+    if (!wide && wv != 0) return;
+  } else {
+    const int groups = (a.rows + kCombineWays - 1) / kCombineWays;
+    hk = blockIdx.x / groups;
+    row = (blockIdx.x - hk * groups) * kCombineWays + wv;
+  }
+  const int way = wide ? wv : 0, ways = wide ? kCombineWays : 1;
+  const bool valid = row < a.rows;                    // wave-uniform
+  const long sstride = (long)a.hk * a.rows;
+  float mu = kNegInf, Z = 0.f;
+  float acc[8] = {};
+  if (valid && way < n) {
+    const float *pl = a.part_lse + ((long)(slot0 + way) * a.hk + hk) * a.rows + row;
+    const uint16_t *po = a.part_o + (((long)(slot0 + way) * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
+    merge_splits<8>(pl, po, ways * sstride, (n - way + ways - 1) / ways, mu, Z, acc);
+  }
+  if (wide) {
+    if (lane == 0) {
+      st_mu[wv] = mu;
+      st_z[wv] = Z;
+    }
+    *(f32x4 *)&st_acc[wv][lane * 8] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4 *)&st_acc[wv][lane * 8 + 4] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int j = 1; j < kCombineWays; ++j) {
+      const f32x4 lo = *(const f32x4 *)&st_acc[j][lane * 8];
+      const f32x4 hi = *(const f32x4 *)&st_acc[j][lane * 8 + 4];
+      const float accj[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      fold_state(mu, Z, acc, st_mu[j], st_z[j], accj);
+    }
+  }
+  if (!valid) return;
+  const int qi = row / a.group;
+  const int h = hk * a.group + (row - qi * a.group);
+  if (a.sinks) {
+    const float zero[8] = {};
+    fold_state(mu, Z, acc, a.sinks[h], 1.f, zero);
   }
   const float inv = Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
   uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + lane * 8;
@@ -924,8 +985,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  const dim3 grid(a.batch, a.hk * ((a.rows + 3) / 4));
-  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(256), 0, stream, a);
+  const dim3 grid(combine_per_row(a) ? a.hk * a.rows : a.hk * ((a.rows + kCombineWays - 1) / kCombineWays),
+                  a.batch);
+  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(kCombineWays * 64), 0, stream, a);
   return hipGetLastError();
 }
 
