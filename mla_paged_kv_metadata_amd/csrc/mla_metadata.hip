@@ -75,49 +75,34 @@ __device__ __forceinline__ int upper_index(const long long *pref, int n, long lo
   return lo;
 }
 
-__global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restrict__ seqlens, int B,
-                                                           int num_parts, int fixed_cost,
-                                                           int32_t *__restrict__ tile_md,
-                                                           int32_t *__restrict__ num_splits) {
-  extern __shared__ long long smem[];
-  long long *pref = smem;                // B + 1 entries: cost prefix
-  long long *cnt = smem + (B + 1);       // B + 1 entries: split-count prefix
-  long long *tmp = smem + 2 * (B + 1);   // kT entries
+template <typename T>
+__device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
+                                          int32_t *__restrict__ tile_md, int32_t *__restrict__ num_splits,
+                                          long long *pref, long long *cnt, long long *tmp) {
   const int tid = threadIdx.x;
-  const long long fc = fixed_cost;
+  const T fc = fixed_cost;
+  const T total = (T)pref[B];
+  const T P = num_parts;
+  const T W = max((T)1, (total + P - 1) / P);                 // most units of one part
+  auto bound = [&](T p) -> T { return p * total / P; };
+  auto part_of = [&](T u) -> T { return ((u + 1) * P - 1) / total; };   // u < total
 
-  for (int b = tid; b < B; b += kT) pref[b] = fc + ceil_div(max(seqlens[b], 0), kPage);
-  __syncthreads();
-  block_exclusive_scan(pref, B, tmp);
-  const long long total = pref[B];
-  const long long P = num_parts;
-  const long long W = max(1LL, ceil_div(total, P));          // most units of one part
-  auto bound = [&](long long p) -> long long { return p * total / P; };
-  auto part_of = [&](long long u) -> long long { return ((u + 1) * P - 1) / total; };   // u < total
-
-  // Splits of b = distinct parts owning its page units.  With total >= P every
-  // part owns a unit, so that is a difference of part indices; otherwise each
-  // unit is a part of its own.
   for (int b = tid; b < B; b += kT) {
-    const long long nblk = pref[b + 1] - pref[b] - fc;
-    const long long s = pref[b] + fc;                       // first page unit of b
+    const T nblk = (T)(pref[b + 1] - pref[b]) - fc;
+    const T s = (T)pref[b] + fc;                            // first page unit of b
     cnt[b] = nblk <= 0 ? 1 : (total >= P ? part_of(s + nblk - 1) - part_of(s) + 1 : nblk);
   }
   __syncthreads();
   block_exclusive_scan(cnt, B, tmp);
   for (int b = tid; b <= B; b += kT) num_splits[b] = (int32_t)cnt[b];
 
-  // Row p in closed form.  Part p works on sequence b when it owns one of
-  // b's page units [s_b, s_b + nblk_b), or, for b without pages, b's first
-  // unit.  Its first sequence is the one holding its first unit or the next
-  // one; its last is the one holding its last unit or the one before.
   for (int p = tid; p < num_parts; p += kT) {
     int32_t *row = tile_md + (size_t)p * 8;
-    const long long u0 = bound(p), u1 = bound(p + 1);
+    const T u0 = bound(p), u1 = bound(p + 1);
     auto works = [&](int b) -> bool {
-      const long long nblk = pref[b + 1] - pref[b] - fc, s = pref[b] + fc;
+      const T nblk = (T)(pref[b + 1] - pref[b]) - fc, s = (T)pref[b] + fc;
       if (nblk > 0) return s < u1 && s + nblk > u0;
-      return u0 <= pref[b] && pref[b] < u1;
+      return u0 <= (T)pref[b] && (T)pref[b] < u1;
     };
     int b0 = -1, b1 = -1;
     if (u0 < u1) {
@@ -134,17 +119,39 @@ __global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restr
       row[0] = -1; row[1] = 0; row[2] = -1; row[3] = 0; row[4] = 0; row[7] = 0;
       continue;
     }
-    const long long n0 = pref[b0 + 1] - pref[b0] - fc, s0 = pref[b0] + fc;
-    const long long n1 = pref[b1 + 1] - pref[b1] - fc, s1 = pref[b1] + fc;
-    long long k0 = 0;
+    const T n0 = (T)(pref[b0 + 1] - pref[b0]) - fc, s0 = (T)pref[b0] + fc;
+    const T n1 = (T)(pref[b1 + 1] - pref[b1]) - fc, s1 = (T)pref[b1] + fc;
+    T k0 = 0;
     if (n0 > 0) k0 = total >= P ? p - part_of(s0) : max(u0, s0) - s0;
     row[0] = b0;
-    row[1] = n0 > 0 ? (int32_t)max(0LL, u0 - s0) : 0;
+    row[1] = n0 > 0 ? (int32_t)max((T)0, u0 - s0) : 0;
     row[2] = b1;
     row[3] = n1 > 0 ? (int32_t)min(n1, u1 - s1) : 0;
     row[4] = (int32_t)k0;
     row[7] = b1 - b0 + 1;
   }
+}
+
+__global__ __launch_bounds__(kT) void mla_metadata_kernel(const int32_t *__restrict__ seqlens, int B,
+                                                           int num_parts, int fixed_cost,
+                                                           int32_t *__restrict__ tile_md,
+                                                           int32_t *__restrict__ num_splits) {
+  extern __shared__ long long smem[];
+  long long *pref = smem;                // B + 1 entries: cost prefix
+  long long *cnt = smem + (B + 1);       // B + 1 entries: split-count prefix
+  long long *tmp = smem + 2 * (B + 1);   // kT entries
+  const int tid = threadIdx.x;
+  const long long fc = fixed_cost;
+
+  for (int b = tid; b < B; b += kT) pref[b] = fc + ceil_div(max(seqlens[b], 0), kPage);
+  __syncthreads();
+  block_exclusive_scan(pref, B, tmp);
+  // The closed forms multiply a unit index by num_parts: 32-bit arithmetic
+  // when that product stays below 2^31 (the common case), else 64-bit.
+  if ((pref[B] + 1) * (long long)num_parts < (1LL << 31))
+    fill_rows<int>(B, num_parts, fixed_cost, tile_md, num_splits, pref, cnt, tmp);
+  else
+    fill_rows<long long>(B, num_parts, fixed_cost, tile_md, num_splits, pref, cnt, tmp);
 }
 
 }  // namespace

@@ -67,3 +67,18 @@ def test_scheduler_kernel_matches_schedule_rule(gpu_lib, parts, fc):
     assert np.array_equal(ns.cpu().numpy(), ref_ns)
     assert np.array_equal(md.cpu().numpy(), ref_md)
     check_schedule(md.cpu().numpy(), ns.cpu().numpy(), w.cache_seqlens, parts, fc)
+
+
+@pytest.mark.parametrize("parts", [1100, 3])
+def test_scheduler_kernel_on_huge_lengths(gpu_lib, parts):
+    """About 2.1M page units: times 1100 parts that passes 2^31 (the kernel's
+    64-bit path); 3 parts stays on the 32-bit path.  The table needs only
+    cache_seqlens, so no cache is allocated."""
+    L = np.array([1 << 24] * 7 + [5, 0, (1 << 24) + 1, 64], dtype=np.int32)
+    sl = torch.from_numpy(L).cuda()
+    import mla_paged_kv_metadata_amd as mla
+    md, ns = mla.mla_get_metadata(sl, 128, 1, num_parts=parts, fixed_cost=4)
+    torch.cuda.synchronize()
+    ref_md, ref_ns = schedule(L, parts, 4)
+    assert np.array_equal(ns.cpu().numpy(), ref_ns)
+    assert np.array_equal(md.cpu().numpy(), ref_md)
