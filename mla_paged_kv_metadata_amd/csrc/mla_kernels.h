@@ -10,7 +10,7 @@ constexpr int kHeadDim = 576;
 constexpr int kHeadDimV = 512;
 constexpr int kPage = 64;
 constexpr int kRowsPerTile = 128;     // rows (query heads x s_q) per decode workgroup
-constexpr int kMetaThreads = 1024;
+constexpr int kMetaThreads = 256;
 
 struct DecodeArgs {
   const uint16_t *q;          // bf16 bits [B][s_q][Hq][q_stride]
