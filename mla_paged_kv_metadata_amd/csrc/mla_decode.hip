@@ -490,23 +490,6 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Writes this wave's 32 x 512 result rows (times f, rounded to bf16) to
-// global memory, coalesced: the O^T accumulators hold one row per lane and
-// 4-dim pieces, so the tile is transposed through LDS (`stage`, private to
-// the wave) in four rounds of 128 dims that alternate between two 32-row
-// regions, so one round's read-back and stores overlap the next round's
-// conversion.  Per round, pairs of 4-dim pieces are merged into 16-byte
-// chunks across lane ^ 32 with v_permlane32_swap; the 16-byte row padding
-// makes both the column writes (16 rows, one chunk) and the row reads (one
-// row, 16 chunks) conflict-free.  Each read-back instruction covers four
-// 256-byte row pieces, which go out as one contiguous 16-byte store per lane.
-//   row_idx : this lane's destination row index in units of 512 elements
-//             (lanes 0..31 hold rows 0..31 of the wave)
-//   nrows   : number of valid rows of the wave (0..32)
-constexpr int kStageRow = 272;                     // 128 dims (256 B) + 16 B padding
-constexpr int kStageRegion = 32 * kStageRow;       // one round's rows
-constexpr int kStageWave = 2 * kStageRegion;       // two alternating regions per wave
-static_assert(4 * kStageWave <= kPageBytes, "the four waves' staging fits in one page buffer");
 // The lane index is re-derived here through an opaque instruction: the
 // lane-dependent addresses below are then computed where they are used
 // instead of being hoisted out of the sequence loop, where they would only
@@ -542,49 +525,36 @@ __device__ __forceinline__ RowCoord row_coord(int wrow0, int rows, int group, in
   return c;
 }
 
+// Writes this wave's 32 x 512 result rows (times f, rounded to bf16) to
+// global memory straight from the accumulators: in O^T tile t a lane holds
+// its row's dims in 4-dim pieces (8q + 4*(lane/32) .. +3); v_permlane32_swap
+// with lane ^ 32 merges piece pairs into whole 16-byte chunks, so one store
+// instruction writes 32 bytes (two adjacent chunks) of each of the 32 rows.
+// (Staging the tile through LDS for longer contiguous runs measured no
+// faster, and LDS is the page loop's busiest unit.)
+//   row_idx : this lane's destination row index in units of 512 elements
+//             (lanes l and l + 32 hold row l % 32 of the wave)
+//   nrows   : number of valid rows of the wave (0..32)
 __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
-                                           int nrows, LDS_AS uint8_t *stage) {
+                                           int nrows) {
   const int lane = lane_id_here();
-  const int r = lane & 31, hl = lane >> 5, g = lane >> 4, c = lane & 15;
+  const int r = lane & 31, hl = lane >> 5;
+  uint16_t *row = base + (long)row_idx * kHeadDimV + 8 * (1 - hl);
+  const bool full = nrows == 32;                      // wave-uniform
 #pragma unroll
-  for (int R = 0; R < 4; ++R) {
-    LDS_AS uint8_t *region = stage + (R & 1) * kStageRegion;
-    LDS_AS uint8_t *wr = region + r * kStageRow + (hl ? 0 : 16);   // lanes < 32 write the odd chunk of a pair
+  for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int t = 4 * R + tt;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        // piece q holds dims 8q + 4*hl .. +3 of tile t
-        const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);   // q = 2pp
-        const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
-        const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);   // q = 2pp + 1
-        const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
-        // After the swap lanes < 32 hold chunk q = 2pp + 1, lanes >= 32 chunk 2pp.
-        const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
-        *(LDS_AS u32x4 *)(wr + (4 * tt + 2 * pp) * 16) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-      }
-    }
-    // Read-backs (row 4k + g, chunk c) and the rows' destinations, then the
-    // stores; a full tile takes a branch-free path, so that the LDS reads and
-    // lane exchanges go out together and are awaited once.
-    const LDS_AS uint8_t *rd = region + g * kStageRow + c * 16;
-    u32x4 v[8];
-    int dst_row[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v[k] = *(const LDS_AS u32x4 *)(rd + 4 * k * kStageRow);
-      dst_row[k] = __builtin_amdgcn_ds_bpermute((4 * k + g) << 2, row_idx);
-    }
-    uint16_t *col = base + R * 128 + c * 8;
-    if (nrows == 32) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) *(u32x4 *)(col + (long)dst_row[k] * kHeadDimV) = v[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (4 * k + g < nrows) *(u32x4 *)(col + (long)dst_row[k] * kHeadDimV) = v[k];
+    for (int pp = 0; pp < 2; ++pp) {
+      // piece q holds dims 8q + 4*hl .. +3 of tile t
+      const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);   // q = 2pp
+      const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
+      const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);   // q = 2pp + 1
+      const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
+      // After the swap lanes < 32 hold chunk 2pp + 1 (dims 32t + 16pp + 8 ..),
+      // lanes >= 32 chunk 2pp (dims 32t + 16pp ..).
+      const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+      if (full || r < nrows) *(u32x4 *)(row + 32 * t + 16 * pp) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     }
   }
 }
@@ -800,10 +770,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
 
     // Epilogue.  A sequence with one split writes out / lse; otherwise the
     // split writes its normalised output (bf16) and lse to its partial slot,
-    // which is its split number num_splits[b] + k.  The results are staged
-    // through the buffer of the split's last page (free once every wave is
-    // past the barriers above; fp8: the bf16 page), never through bufs[cur],
-    // which may be receiving the next split's first page.
+    // which is its split number num_splits[b] + k.
     if (active) {
       const bool direct = nsplit <= 1;
       const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
@@ -824,11 +791,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const float lse_v = lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
-      LDS_AS uint8_t *stage = (kFp8 ? page0 : bufs[cur ^ 1]) + wave * kStageWave;
       const float v_scale = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
       store_rows(o, direct ? inv * v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow,
-                 max(0, min(32, uniform_here(a.rows) - wrow0)),
-                 stage);
+                 max(0, min(32, uniform_here(a.rows) - wrow0)));
       if (lane_id_here() < 32 && c.row < a.rows) {
         if (direct) a.lse[((long)b * a.hq + c.h) * a.s_q + c.qi] = lse_v;
         else a.part_lse[prow] = lse_v;
