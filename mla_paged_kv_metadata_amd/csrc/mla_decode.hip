@@ -211,11 +211,6 @@ __device__ __forceinline__ void dma_fp8_dispatch(const PageSrc &p, LDS_AS uint8_
   }
 }
 
-// Two floats that hold bf16-exact values -> packed bf16 pair (truncation is exact here).
-__device__ __forceinline__ unsigned pack_bf16_exact(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
 // Widen the staged fp8 page into the bf16 page layout.  Thread (wave, lane)
 // owns staging chunks of instruction I = 4k + wave: token 16*wave + lane/4,
 // fp8 chunk 4k + lane%4 -> bf16 chunks 2c and 2c + 1 of that token.  Rows
@@ -231,10 +226,12 @@ __device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_
     unsigned w[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
-      w[2 * i] = keep ? pack_bf16_exact(lo[0], lo[1]) : 0u;
-      w[2 * i + 1] = keep ? pack_bf16_exact(hi[0], hi[1]) : 0u;
+      // e4m3fn -> bf16 pairs in one instruction each (scale 1: exact, every
+      // e4m3fn value is a bf16 value).
+      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, false);
+      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, true);
+      w[2 * i] = keep ? __builtin_bit_cast(unsigned, lo) : 0u;
+      w[2 * i + 1] = keep ? __builtin_bit_cast(unsigned, hi) : 0u;
     }
     *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c) * 16) = u32x4{w[0], w[1], w[2], w[3]};
     *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c + 1) * 16) = u32x4{w[4], w[5], w[6], w[7]};
