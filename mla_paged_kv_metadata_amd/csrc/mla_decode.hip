@@ -30,10 +30,12 @@
 //    belong to one head, so the softmax rescale is a per-lane scalar.
 //  * Softmax runs in base 2 with log2(e) folded into the scale.
 //  * A sequence with one split writes bf16 out / fp32 lse directly; a split
-//    sequence writes fp32 partials (O/l, lse) that the combine kernel merges.
-//  * fp8 (e4m3fn) caches are DMA'd as codes into a staging buffer and
-//    widened exactly to bf16 in LDS (every e4m3fn value is a bf16 value);
-//    the fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
+//    sequence writes bf16 partials (O/l) and fp32 lse that the combine
+//    kernel merges.
+//  * fp8 (e4m3fn) caches stay as codes in LDS (half the bytes of a bf16
+//    page); each 8-code operand fragment is converted exactly to bf16 in
+//    registers just before its MFMA (every e4m3fn value is a bf16 value).
+//    The fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
 //    softmax_scale and v_scale.
 #include "mla_kernels.h"
 
@@ -47,6 +49,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -160,17 +164,46 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid,
   }
 }
 
-// HBM -> LDS copy of one fp8 page (64 rows x 576 B) into staging: slot
-// I = 4 * (column group of 64 B) + token block (16 tokens); wave w copies
-// token block w, instruction k covering column group k (group 8, the rope
-// columns, from the kRope rows of a split cache).
+// LDS layout of an fp8 page (64 tokens x 576 codes): nine column groups of
+// 64 B, group g at 4096 g holding 64 B of every token at 64 t; within a
+// token's 64 B, 16-byte chunk j sits at position j ^ ((t >> 2) & 3).  Both
+// 8-byte operand reads are then conflict-free: 16 tokens reading one 8-byte
+// half-chunk (K of S^T) cover (t % 4, position, half) without repeats, and so
+// do the transposing reads of V^T (tokens base + {0..3, 8..11}, two halves).
+// HBM -> LDS copy: slot I = 4 * group + token block (16 tokens), wave w
+// copies token block w, instruction k covering group k (group 8, the rope
+// columns, from the kRope rows of a split cache); lane l writes slot bytes
+// 16 l, i.e. token 16 w + l / 4 at position l % 4, so it fetches chunk
+// (l % 4) ^ ((l / 16) % 4) of the group.
 template <bool kSplit>
 __device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *tok0, const uint8_t *rope0, int tok_stride,
                                                 int rope_stride, int wave, int lane) {
   PageSrc p;
-  p.even = p.odd = tok0 + (16 * wave + (lane >> 2)) * tok_stride + (lane & 3) * 16;
-  p.rope_even = p.rope_odd = kSplit ? rope0 + (16 * wave + (lane >> 2)) * rope_stride + (lane & 3) * 16 : nullptr;
+  const int chunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+  p.even = p.odd = tok0 + (16 * wave + (lane >> 2)) * tok_stride + chunk;
+  p.rope_even = p.rope_odd = kSplit ? rope0 + (16 * wave + (lane >> 2)) * rope_stride + chunk : nullptr;
   return p;
+}
+
+// Zero tokens nvalid..63 of an fp8 page in LDS (cache rows past a sequence's
+// end may hold NaN codes, and 0 * NaN would poison the PV product).
+__device__ __forceinline__ void zero_tail_rows_fp8(LDS_AS uint8_t *page, int nvalid, int tid) {
+  const int first = nvalid * kF8RowChunks;
+  for (int i = first + tid; i < kPage * kF8RowChunks; i += kThreads) {
+    const int t = i / kF8RowChunks, c = i - t * kF8RowChunks;
+    *(LDS_AS u32x4 *)(page + 4096 * (c >> 2) + 64 * t + 16 * (c & 3)) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Eight e4m3fn codes -> eight bf16 (exact: every e4m3fn value is a bf16
+// value), two per instruction.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                          __builtin_bit_cast(unsigned, c), __builtin_bit_cast(unsigned, d)});
 }
 template <bool kSplit, int k>
 __device__ __forceinline__ void dma_fp8_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
@@ -211,33 +244,6 @@ __device__ __forceinline__ void dma_fp8_dispatch(const PageSrc &p, LDS_AS uint8_
   }
 }
 
-// Widen the staged fp8 page into the bf16 page layout.  Thread (wave, lane)
-// owns staging chunks of instruction I = 4k + wave: token 16*wave + lane/4,
-// fp8 chunk 4k + lane%4 -> bf16 chunks 2c and 2c + 1 of that token.  Rows
-// past the sequence end (t >= nvalid) are written as zeros.
-__device__ __forceinline__ void widen_fp8_page(const LDS_AS uint8_t *stage, LDS_AS uint8_t *page, int wave,
-                                               int lane, int nvalid) {
-  const int t = 16 * wave + (lane >> 2);
-  const bool keep = t < nvalid;
-#pragma unroll
-  for (int k = 0; k < kF8PageLoads; ++k) {
-    const int c = 4 * k + (lane & 3);
-    const u32x4 v = *(const LDS_AS u32x4 *)(stage + ((4 * k + wave) * 64 + lane) * 16);
-    unsigned w[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // e4m3fn -> bf16 pairs in one instruction each (scale 1: exact, every
-      // e4m3fn value is a bf16 value).
-      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, false);
-      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, true);
-      w[2 * i] = keep ? __builtin_bit_cast(unsigned, lo) : 0u;
-      w[2 * i + 1] = keep ? __builtin_bit_cast(unsigned, hi) : 0u;
-    }
-    *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c) * 16) = u32x4{w[0], w[1], w[2], w[3]};
-    *(LDS_AS u32x4 *)(page + pos_bf16(t, 2 * c + 1) * 16) = u32x4{w[4], w[5], w[6], w[7]};
-  }
-}
-
 // One 64-token page for this wave's 32 rows, processed as two 32-token
 // halves: scores, online softmax, PV.
 //   key0 : sequence index of the page's first token; nvis: keys this lane's row may see.
@@ -271,11 +277,18 @@ __device__ __forceinline__ void mfma_zero_all(f32x16 (&o)[kOTiles]) {
 // 32x32 MFMA destination may not overlap its A/B sources).  mfma_qk_drain
 // supplies the wait states between the last matrix-core write of S^T and
 // its first VALU read (19 > the 8-pass XDL requirement).
+// kFresh: the A operand was just written by VALU (a converted fp8
+// fragment); the compiler does not see into the asm, so the 2 wait states a
+// VALU-written VGPR needs before an MFMA reads it are supplied here.
+template <bool kFresh = false>
 __device__ __forceinline__ void mfma_qk_first(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+  if constexpr (kFresh) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
 }
+template <bool kFresh = false>
 __device__ __forceinline__ void mfma_qk(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+  if constexpr (kFresh) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_qk_drain(f32x16 &s) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s));
@@ -299,7 +312,7 @@ __device__ __forceinline__ float sum_across_halves(float v) {
 // address unit drains them.
 struct NextPage {
   PageSrc src;                // this lane's source addresses of the next page
-  LDS_AS uint8_t *dst;        // its LDS (bf16 page or fp8 staging) buffer
+  LDS_AS uint8_t *dst;        // its LDS page buffer
   int wave;
   bool valid;                 // workgroup-uniform
 };
@@ -339,16 +352,47 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   const LDS_AS uint8_t *va_even = pg + la + 64 * t1, *va_odd = pg + la + 64 * (1 - t1);
   const LDS_AS uint8_t *vb_even = pg + lb + 64 * t1, *vb_odd = pg + lb + 64 * (1 - t1);
 
+  // fp8 page (the layout of page_src_fp8): K of token r, codes 16 ks + 8 hl
+  // .. +7 at 4096 (ks / 4) + 64 r + 16 ((ks % 4) ^ ((r / 4) % 4)) + 8 hl
+  // (+2048 for tile 1): four lane bases.  V^T by 8-bit transposing reads: in
+  // each 16-lane group G, output lane i gets byte i % 8 of the 8-byte rows
+  // loaded by lanes 2 e + i / 8 (e = 0..7, its k-slots); for the k-slot order
+  // of P^T (slot e of lane half h is token 8 (e / 4) + 4 h + e % 4 of the
+  // k-step) source lane (G, s) loads token 16 ks + 8 (s / 8) + 4 (G / 2) +
+  // (s / 2) % 4, codes 32 mt + 16 (G % 2) + 8 (s % 2) .. +7: two lane bases
+  // (even / odd mt) plus immediates.
+  const int f_sw = (r >> 2) & 3;
+  const LDS_AS uint8_t *kb8[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) kb8[v] = pg + 64 * r + 16 * (v ^ f_sw) + 8 * hl;
+  const int fa = s16 >> 3, fb = g >> 1, fc = (s16 >> 1) & 3;
+  const int f_lane = 64 * (8 * fa + 4 * fb + fc) + 8 * (s16 & 1);
+  const LDS_AS uint8_t *v8[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) v8[par] = pg + f_lane + 16 * ((2 * par + (g & 1)) ^ (2 * fa + fb));
+
   // LDS operand loads run ahead of their MFMAs (software pipeline); loads
-  // complete in order, so each MFMA waits only for its own operand.
-  auto kload = [&](int ks, int tile) -> bf16x8 {
-    return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + tile * 4096);
+  // complete in order, so each MFMA waits only for its own operand.  An fp8
+  // operand stays as 8 codes (two VGPRs) until just before its MFMA.
+  auto kload = [&](int ks, int tile) {
+    if constexpr (kFp8) return *(const LDS_AS u32x2 *)(kb8[ks & 3] + 4096 * (ks >> 2) + 2048 * tile);
+    else return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + tile * 4096);
   };
-  auto vload = [&](int step, bf16x4 &lo, bf16x4 &hi) {
+  auto vload = [&](int step) {
     const int ks = step >> 4, mt = step & 15;         // k-step of 16 tokens, 32-dim output tile
-    const int ofs = 8192 * (mt >> 1) + 2048 * ks;
-    lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
-    hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
+    if constexpr (kFp8) {
+      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (LDS_AS v2i32 *)(v8[mt & 1] + 4096 * (mt >> 1) + 1024 * ks)));
+    } else {
+      const int ofs = 8192 * (mt >> 1) + 2048 * ks;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto cook = [&](auto raw) -> bf16x8 {
+    if constexpr (kFp8) return fp8x8_to_bf16(raw);
+    else return raw;
   };
 
   // Online softmax of one 32-token tile, in kSoftPieces pieces that are
@@ -410,7 +454,7 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // chain.
   constexpr int kPre = 4;
   constexpr int kDmaEvery = 2 * kKSteps / (kFp8 ? kF8PageLoads : kPageLoads);   // 4 (bf16) or 8 (fp8)
-  bf16x8 kf[kPre];
+  decltype(kload(0, 0)) kf[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) kf[i] = kload(i, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -421,8 +465,8 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // instruction of the next page.
   auto qk_step = [&](f32x16 &sc, int tile, int ks) {
     const int g = tile * kKSteps + ks, sl = g % kPre;
-    if (ks == 0) mfma_qk_first(sc, kf[sl], qf[0]);
-    else mfma_qk(sc, kf[sl], qf[ks]);
+    if (ks == 0) mfma_qk_first<kFp8>(sc, cook(kf[sl]), qf[0]);
+    else mfma_qk<kFp8>(sc, cook(kf[sl]), qf[ks]);
     if (g + kPre < 2 * kKSteps) kf[sl] = kload((g + kPre) % kKSteps, (g + kPre) / kKSteps);
     if (nx.valid && g % kDmaEvery == 0) {
       if (kFp8) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
@@ -448,17 +492,16 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   }
   // First V^T operands.
   constexpr int kVPre = 4;
-  bf16x4 vlo[kVPre], vhi[kVPre];
+  decltype(vload(0)) vraw[kVPre];
 #pragma unroll
-  for (int i = 0; i < kVPre; ++i) vload(i, vlo[i], vhi[i]);
+  for (int i = 0; i < kVPre; ++i) vraw[i] = vload(i);
 
   // O^T += V^T P^T over 4 k-steps x 16 dim tiles; the tile-1 softmax runs
   // under the first two k-steps (tile 0's P), which do not need it.
   auto pv_step = [&](int step) {
     const int sl = step % kVPre;
-    const bf16x8 av = __builtin_shufflevector(vlo[sl], vhi[sl], 0, 1, 2, 3, 4, 5, 6, 7);
-    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[step >> 4], o[step & 15], 0, 0, 0);
-    if (step + kVPre < 4 * kOTiles) vload(step + kVPre, vlo[sl], vhi[sl]);
+    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cook(vraw[sl]), pb[step >> 4], o[step & 15], 0, 0, 0);
+    if (step + kVPre < 4 * kOTiles) vraw[sl] = vload(step + kVPre);
   };
   constexpr int kSoftCN = 2 * kOTiles - 2;
 #pragma unroll
@@ -568,10 +611,8 @@ template <bool kFp8, bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
-  // bf16: two page buffers.  fp8: one bf16 page + two fp8 staging buffers.
-  LDS_AS uint8_t *const bufs[2] = {smem, smem + kPageBytes};
-  LDS_AS uint8_t *const stages[2] = {smem + kPageBytes, smem + kPageBytes + kF8PageBytes};
-  LDS_AS uint8_t *const page0 = smem;
+  // Two page buffers: 72 KiB each for bf16, 36 KiB each for fp8.
+  LDS_AS uint8_t *const bufs[2] = {smem, smem + (kFp8 ? kF8PageBytes : kPageBytes)};
   volatile LDS_AS int *rerun_flag = (volatile LDS_AS int *)(smem + 2 * kPageBytes);
 
   const int tid = threadIdx.x;
@@ -652,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int hi0 = seq_end(b0, nblk0);
     if (hi0 > first0) {                               // then the split's first page is first0
       const PageSrc src = src_of(__builtin_amdgcn_readfirstlane(bt_pref));
-      if (kFp8) dma_page_fp8<kSplit>(src, stages[0], wave);
+      if (kFp8) dma_page_fp8<kSplit>(src, bufs[0], wave);
       else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
     }
@@ -709,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       for (int pass = 0;; ++pass) {
         bool need = false;
         if (!have_first) {
-          if (kFp8) dma_page_fp8<kSplit>(src_of(page_of(lo)), stages[cur], wave);
+          if (kFp8) dma_page_fp8<kSplit>(src_of(page_of(lo)), bufs[cur], wave);
           else dma_page_bf16<kSplit>(src_of(page_of(lo)), bufs[cur], wave);
         }
         have_first = false;
@@ -719,23 +760,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           wait_vmcnt<0>();
           __syncthreads();
           const int nvalid = min(kPage, L - j * kPage);
-          if (!kFp8 && nvalid < kPage) {            // the sequence's last, partial page
-            zero_tail_rows(bufs[cur], nvalid, tid);
+          if (nvalid < kPage) {                     // the sequence's last, partial page
+            if (kFp8) zero_tail_rows_fp8(bufs[cur], nvalid, tid);
+            else zero_tail_rows(bufs[cur], nvalid, tid);
             __syncthreads();
           }
           NextPage nx;
           nx.valid = j + 1 < hi || next_has_pages;
           nx.src = src_of(j + 1 < hi ? page_of(j + 1) : next_pg);
-          nx.dst = kFp8 ? stages[cur ^ 1] : bufs[cur ^ 1];
+          nx.dst = bufs[cur ^ 1];
           nx.wave = wave;
-          const LDS_AS uint8_t *pg;
-          if (kFp8) {
-            widen_fp8_page(stages[cur], page0, wave, lane, nvalid);
-            __syncthreads();
-            pg = page0;
-          } else {
-            pg = bufs[cur];
-          }
+          const LDS_AS uint8_t *pg = bufs[cur];
           if (active) {
             need |= attend_page<kFp8, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
                                       (j + 1) * kPage > nvis_min, nx);
@@ -933,8 +968,7 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  const size_t smem = 2 * (size_t)kPageBytes + 16;   // pages (or page + fp8 staging) + restart flag
-  static_assert(kPageBytes + 2 * kF8PageBytes == 2 * kPageBytes, "fp8 staging fills the second page slot");
+  const size_t smem = 2 * (size_t)kPageBytes + 16;   // two pages (bf16 size) + restart flag
   const dim3 grid(a.num_parts, a.row_tiles * a.hk);   // one persistent workgroup per part
   auto launch = [&](auto kernel) -> hipError_t {
     hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
