@@ -71,3 +71,58 @@ def test_graph_replays_match_eager(gpu_lib):
     g.replay()
     torch.cuda.synchronize()
     compare(w2, out, lse, run_oracle(w2), label="replay with new lengths")
+
+
+def test_graph_replays_with_ext_inputs(gpu_lib):
+    """fp8 split cache and split query, sinks and device scales inside the graph:
+    replays match eager bit for bit, and a new bmm1 scale written into its
+    device buffer between replays is picked up (the eager call with that scale
+    as a host value gives the same bits)."""
+    w = make_workload(seqlens=[900, 3, 0, 1500, 65], num_heads_q=64, s_q=2, causal=True, kv_dtype="fp8_e4m3fn",
+                      seed=79)
+    q, kv, bt, sl = to_gpu(w)
+    dev = q.device
+    P = 16
+    s1, s2 = scales(w)
+    kv_nope, kv_rope = kv[..., :DV].contiguous(), kv[..., DV:].contiguous()
+    q_nope, q_rope = q[..., :DV].contiguous(), q[..., DV:].contiguous()
+    sinks = torch.linspace(-1.0, 2.0, 64, device=dev)
+    b1 = torch.tensor([s1], dtype=torch.float32, device=dev)
+    b2 = torch.tensor([s2], dtype=torch.float32, device=dev)
+    md = torch.empty((P, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, 2, 64, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, 64, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty((mla.mla_workspace_bytes(w.batch, 2, 64, 1, DV, P),), dtype=torch.uint8, device=dev)
+    ext = dict(sinks=sinks, bmm1_scale_tensor=b1, bmm2_scale_tensor=b2, kv_rope=kv_rope, q_rope=q_rope)
+
+    def step():
+        mla.mla_get_metadata(sl, w.heads_per_head_k, 1, num_parts=P, tile_md=md, num_splits=ns)
+        mla.mla_decode_fwd(q_nope, kv_nope, bt, sl, DV, md, ns, causal=True, out=out, lse=lse, workspace=ws, **ext)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {rep} differs from eager"
+    b1.fill_(s1 * 0.5)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    o2, l2 = mla.mla_decode_fwd(q, kv, bt, sl, DV, md, ns, softmax_scale=float(b1.item()), v_scale=s2, causal=True,
+                                sinks=sinks)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
