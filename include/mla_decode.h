@@ -48,7 +48,13 @@ extern "C" {
  * 512, qk_rope_head_dim 64). */
 #define MLA_HEAD_DIM 576
 #define MLA_HEAD_DIM_V 512
+/* Tokens per scheduling page: the split-KV metadata counts sequence lengths
+ * and split boundaries in pages of this many tokens, whatever the cache's
+ * block size (FlashMLA interface page: the cache block of 64 tokens). */
 #define MLA_PAGE_BLOCK_SIZE 64
+/* The cache's page_block_size must be a multiple of this (the kernels copy a
+ * block's rows in 16-token slices). */
+#define MLA_PAGE_BLOCK_ALIGN 16
 /* Largest batch the scheduler kernel accepts. */
 #define MLA_MAX_BATCH 8192
 /* Largest rows per KV head (s_q * num_heads_q / num_heads_k). */
@@ -135,7 +141,8 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
  *                  the rest must lie in [0, num_blocks) (not checked: that
  *                  would need a device read).  Cache rows past
  *                  cache_seqlens[b] in a sequence's last block are never read.
- *   cache_seqlens: device int32 [batch], 0 <= L_b <= max_blocks_per_seq * 64.
+ *   cache_seqlens: device int32 [batch],
+ *                  0 <= L_b <= max_blocks_per_seq * page_block_size.
  *   softmax_scale: factor >= 0 on q.k before the softmax (bmm1_scale for an
  *                  fp8 cache; a negative value is UNSUPPORTED).  The Python
  *                  wrapper supplies 1/sqrt(head_dim) when the caller gives
@@ -145,7 +152,8 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
  *                  (bottom-right alignment).  A row with no visible key gets
  *                  out = 0 and lse = -inf.
  *   tile_md, num_parts, num_splits: from mla_get_metadata for these
- *                  cache_seqlens and this head layout (tile_md has num_parts
+ *                  cache_seqlens and this head layout, in 64-token pages
+ *                  for any page_block_size (tile_md has num_parts
  *                  rows; one persistent workgroup per part and 128-row tile
  *                  of each KV head walks its row's run of sequences).
  *   workspace    : device buffer of >= mla_workspace_bytes(...) bytes,
@@ -154,7 +162,9 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
  *   lse          : device fp32 [batch][num_heads_q][s_q], written: natural
  *                  log of sum_t exp(softmax_scale * q.k_t).
  * q head h uses KV head h / (num_heads_q / num_heads_k).
- * Requires head_dim = 576, head_dim_v = 512, page_block_size = 64, a gfx950
+ * Requires head_dim = 576, head_dim_v = 512, page_block_size a positive
+ * multiple of MLA_PAGE_BLOCK_ALIGN (the pages' caches use 64; FlashInfer
+ * MLA page and Ascend ATB MLA page: any page or block size), a gfx950
  * device, and s_q * num_heads_q / num_heads_k <= MLA_MAX_ROWS. */
 int mla_decode_fwd(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
                    const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
@@ -205,8 +215,8 @@ int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int h
  *                ctKV [num_blocks, block_size, kv_heads, 512] and kRope
  *                [num_blocks, block_size, kv_heads, 64]).  When set,
  *                kv_cache holds the 512 latent columns
- *                [num_blocks][64][num_heads_k][512] and kv_rope the 64 rope
- *                columns [num_blocks][64][num_heads_k][64], both of kv_dtype;
+ *                [num_blocks][page_block_size][num_heads_k][512] and kv_rope the 64 rope
+ *                columns [num_blocks][page_block_size][num_heads_k][64], both of kv_dtype;
  *                the block table indexes both.
  *   q_rope     : split query (same page: qNope and qRope).  When set, q holds
  *                [batch][s_q][num_heads_q][512] and q_rope the rope columns,

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
 TILE_MD_INTS = 8
 HEAD_DIM = 576
 HEAD_DIM_V = 512
-PAGE_BLOCK_SIZE = 64
+PAGE_BLOCK_SIZE = 64        # tokens per scheduling page (and the usual cache block)
+PAGE_BLOCK_ALIGN = 16       # a cache's page_block_size must be a multiple of this
 KV_BF16 = 0
 KV_FP8_E4M3FN = 1
 
@@ -192,8 +193,9 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
                    q_rope: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode attention (FlashMLA interface page, flash_mla_with_kvcache).
 
-    q (B, s_q, H_q, 576) bf16; kv_cache (num_blocks, 64, H_k, 576) bf16 or
-    e4m3fn; block_table (B, max_blocks) int32; cache_seqlens (B,) int32.
+    q (B, s_q, H_q, 576) bf16; kv_cache (num_blocks, page_block_size, H_k, 576)
+    bf16 or e4m3fn, page_block_size a multiple of 16 (64 in the pages'
+    caches); block_table (B, max_blocks) int32; cache_seqlens (B,) int32.
     stage: "all" (mla_decode_fwd), or "splits" / "combine" to run one of its
     two kernels (mla_decode_splits / mla_combine_splits; pass the same out,
     lse and workspace to both).
@@ -204,8 +206,9 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
     Optional inputs (mla_decode_fwd_ext; FlashInfer MLA page and Ascend ATB
     MLA page): sinks (H_q,) fp32 per-head sink logits; bmm1_scale_tensor /
     bmm2_scale_tensor (1,) fp32 device scales replacing softmax_scale /
-    v_scale; kv_rope (num_blocks, 64, H_k, 64) with kv_cache then
-    (num_blocks, 64, H_k, 512) (split cache); q_rope (B, s_q, H_q, 64) bf16
+    v_scale; kv_rope (num_blocks, page_block_size, H_k, 64) with kv_cache
+    then (num_blocks, page_block_size, H_k, 512) (split cache); q_rope
+    (B, s_q, H_q, 64) bf16
     with q then (B, s_q, H_q, 512) (split query).
     """
     lib = load_library()

@@ -158,7 +158,8 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   if (softmax_scale < 0.f) return fail(MLA_ERR_UNSUPPORTED, "softmax_scale must be >= 0");
   if (head_dim != MLA_HEAD_DIM) return fail(MLA_ERR_UNSUPPORTED, "head_dim must be 576 (512 latent + 64 rope)");
   if (head_dim_v != MLA_HEAD_DIM_V) return fail(MLA_ERR_UNSUPPORTED, "head_dim_v must be 512");
-  if (page_block_size != MLA_PAGE_BLOCK_SIZE) return fail(MLA_ERR_UNSUPPORTED, "page_block_size must be 64");
+  if (page_block_size % MLA_PAGE_BLOCK_ALIGN)
+    return fail(MLA_ERR_UNSUPPORTED, "page_block_size must be a multiple of 16");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3FN)
     return fail(MLA_ERR_UNSUPPORTED, "kv_dtype must be MLA_KV_BF16 or MLA_KV_FP8_E4M3FN");
   const int group = num_heads_q / num_heads_k;
@@ -198,6 +199,7 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   a.row_tiles = row_tiles((int)rows);
   a.num_parts = num_parts;
   a.num_blocks = num_blocks;
+  a.page_size = page_block_size;
   a.kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3FN;
   a.causal = causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;

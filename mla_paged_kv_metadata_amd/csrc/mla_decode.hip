@@ -38,6 +38,7 @@
 //    The fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
 //    softmax_scale and v_scale.
 #include "mla_kernels.h"
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -125,18 +126,20 @@ struct PageSrc {
   const uint8_t *even, *odd;             // this lane's source for token blocks 2w, 2w + 1 (group 0)
   const uint8_t *rope_even, *rope_odd;   // split cache: the same tokens' rope columns
 };
+// slice0 / rope0: the wave's first token (16 w) of the page in the cache
+// (its 16 tokens are consecutive rows of one cache block).
 template <bool kSplit>
-__device__ __forceinline__ PageSrc page_src_bf16(const uint8_t *tok0, const uint8_t *rope0, int tok_stride,
-                                                 int rope_stride, int wave, int lane) {
+__device__ __forceinline__ PageSrc page_src_bf16(const uint8_t *slice0, const uint8_t *rope0, int tok_stride,
+                                                 int rope_stride, int lane) {
   const int lt = lane >> 3;
   // token t = 16w + 8*(k&1) + lt: h(t) = (lt1, lt2, k&1) -> chunk (lane & 7) ^ h(t)
   PageSrc p;
-  p.even = tok0 + (16 * wave + lt) * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;
-  p.odd = tok0 + (16 * wave + 8 + lt) * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
+  p.even = slice0 + lt * tok_stride + ((lane & 7) ^ swz_h(lt)) * 16;
+  p.odd = slice0 + (8 + lt) * tok_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
   p.rope_even = p.rope_odd = nullptr;
   if (kSplit) {
-    p.rope_even = rope0 + (16 * wave + lt) * rope_stride + ((lane & 7) ^ swz_h(lt)) * 16;
-    p.rope_odd = rope0 + (16 * wave + 8 + lt) * rope_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
+    p.rope_even = rope0 + lt * rope_stride + ((lane & 7) ^ swz_h(lt)) * 16;
+    p.rope_odd = rope0 + (8 + lt) * rope_stride + ((lane & 7) ^ swz_h(lt + 8)) * 16;
   }
   return p;
 }
@@ -176,12 +179,12 @@ __device__ __forceinline__ void zero_tail_rows(LDS_AS uint8_t *page, int nvalid,
 // 16 l, i.e. token 16 w + l / 4 at position l % 4, so it fetches chunk
 // (l % 4) ^ ((l / 16) % 4) of the group.
 template <bool kSplit>
-__device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *tok0, const uint8_t *rope0, int tok_stride,
-                                                int rope_stride, int wave, int lane) {
+__device__ __forceinline__ PageSrc page_src_fp8(const uint8_t *slice0, const uint8_t *rope0, int tok_stride,
+                                                int rope_stride, int lane) {
   PageSrc p;
   const int chunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
-  p.even = p.odd = tok0 + (16 * wave + (lane >> 2)) * tok_stride + chunk;
-  p.rope_even = p.rope_odd = kSplit ? rope0 + (16 * wave + (lane >> 2)) * rope_stride + chunk : nullptr;
+  p.even = p.odd = slice0 + (lane >> 2) * tok_stride + chunk;
+  p.rope_even = p.rope_odd = kSplit ? rope0 + (lane >> 2) * rope_stride + chunk : nullptr;
   return p;
 }
 
@@ -607,7 +610,9 @@ __device__ __forceinline__ int xcd_part(int w, int n) {
   return x * q + min(x, r) + i;
 }
 
-template <bool kFp8, bool kSplit>
+// kAnyBlock: the cache's block size is a.page_size (a multiple of 16) rather
+// than the 64 tokens of a page, whose slice arithmetic is then shifts.
+template <bool kFp8, bool kSplit, bool kAnyBlock>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
@@ -642,21 +647,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int elem = kFp8 ? 1 : 2;
   constexpr int kRowDim = kSplit ? kHeadDimV : kHeadDim;   // columns of a kv_cache row
   const int tok_stride = a.hk * kRowDim * elem;
-  const long page_stride = (long)kPage * tok_stride;
   const uint8_t *kv_head = a.kv + (long)hk * kRowDim * elem;
   const int rope_stride = a.hk * (kHeadDim - kHeadDimV) * elem;
   const uint8_t *rope_head = kSplit ? a.kv_rope + (long)hk * (kHeadDim - kHeadDimV) * elem : nullptr;
-  // This lane's copy sources for page pg (index clamped into the pool).
-  auto src_of = [&](int pg) -> PageSrc {
-    const long pc = max(0, min(pg, a.num_blocks - 1));
-    const uint8_t *t0 = kv_head + pc * page_stride;
-    const uint8_t *r0 = kSplit ? rope_head + pc * kPage * rope_stride : nullptr;
-    return kFp8 ? page_src_fp8<kSplit>(t0, r0, tok_stride, rope_stride, wave, lane)
-                : page_src_bf16<kSplit>(t0, r0, tok_stride, rope_stride, wave, lane);
+  // Pages of the kernel are 64 tokens; cache blocks hold bs tokens (a
+  // multiple of 16), so this wave's 16-token slice of page j, tokens
+  // 64 j + 16 w .., is rows (64 j + 16 w) % bs .. of table entry
+  // (64 j + 16 w) / bs.
+  const int bs = kAnyBlock ? a.page_size : kPage;
+  auto slice_tok = [&](int j) { return j * kPage + 16 * wave; };
+  // This lane's copy sources for the slice starting at row `row` of cache
+  // block blk (index clamped into the pool).
+  auto src_of = [&](int blk, int row) -> PageSrc {
+    const long pc = (long)max(0, min(blk, a.num_blocks - 1)) * bs + row;
+    const uint8_t *t0 = kv_head + pc * tok_stride;
+    const uint8_t *r0 = kSplit ? rope_head + pc * rope_stride : nullptr;
+    return kFp8 ? page_src_fp8<kSplit>(t0, r0, tok_stride, rope_stride, lane)
+                : page_src_bf16<kSplit>(t0, r0, tok_stride, rope_stride, lane);
   };
   // Lengths and page ranges are clamped so that every global address stays
   // inside its buffer whatever the table or cache_seqlens hold.
-  auto seq_len = [&](int b) { return max(0, min(a.seqlens[b], a.max_blocks * kPage)); };
+  auto seq_len = [&](int b) { return (int)max(0L, min((long)a.seqlens[b], (long)a.max_blocks * bs)); };
   auto seq_end = [&](int b, int nblk) { return b == b1 ? max(0, min(md[3], nblk)) : nblk; };
 
   bf16x8 qf[kKSteps];
@@ -677,22 +688,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   int cur = 0;              // buffer that receives / holds the next page to process
   bool have_first = false;  // the first page of the current split is already in flight into it
   // Block-table entries of a split are fetched one split ahead: lane i holds
-  // the page index of the split's page (first + i).
+  // table entry base + i, base = the entry of the split's first token.
   int bt_pref = 0;
   {
     // The part's first block-table entries and length load together, and
     // its q goes out while they are in flight; then its first page.  (Lanes
-    // past the split's pages hold entries that are never used; the index is
+    // past the split's blocks hold entries that are never used; the index is
     // clamped into the table row.)
     const int first0 = max(0, md[1]);
+    const int base0 = first0 * kPage / bs;
     const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
-    bt_pref = bt0[min(first0 + lane, a.max_blocks - 1)];
+    bt_pref = bt0[min(base0 + lane, a.max_blocks - 1)];
     const int len0 = seq_len(b0);
     load_q(b0);
     const int nblk0 = (len0 + kPage - 1) / kPage;
     const int hi0 = seq_end(b0, nblk0);
     if (hi0 > first0) {                               // then the split's first page is first0
-      const PageSrc src = src_of(__builtin_amdgcn_readfirstlane(bt_pref));
+      // (A slice past the sequence's end takes its last block: its rows are
+      // masked, and table entries past the sequence are never used.)
+      const int t = slice_tok(first0);
+      const int k = min(t / bs, (len0 - 1) / bs);     // in [base0, base0 + 3]
+      const PageSrc src = src_of(__builtin_amdgcn_readlane(bt_pref, k - base0), t % bs);
       if (kFp8) dma_page_fp8<kSplit>(src, bufs[0], wave);
       else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
@@ -713,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int32_t *bt = a.block_table + (long)b * a.max_blocks;
     // First page of the next split of this part (page 0 of b + 1), copied
     // while the last page of this split is processed.
-    int next_pg = 0;
+    int next_blk = 0;                                     // block of this wave's slice of page 0 of b + 1
     bool next_has_pages = false;
     const int bt_this = bt_pref;                          // block-table lanes of this split (loaded earlier)
     if (b < b1) {
@@ -722,8 +738,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       next_has_pages = seq_end(b + 1, nblk_n) > 0;
       if (next_has_pages) {
         const int32_t *bt_n = a.block_table + (long)(b + 1) * a.max_blocks;
-        next_pg = bt_n[0];
-        bt_pref = bt_n[min(lane, nblk_n - 1)];            // next split starts at page 0
+        next_blk = bt_n[min(16 * wave / bs, max(0, (Ln + bs - 1) / bs - 1))];
+        bt_pref = bt_n[min(lane, max(0, (Ln + bs - 1) / bs - 1))];   // next split starts at token 0
       }
     }
     if (tid == 0) *rerun_flag = 0;
@@ -735,23 +751,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     mfma_zero_all(o);
 
     if (hi > lo) {
-      // Block-table entries of the split live in one VGPR, lane i holding the
-      // page index of j = bt_base + i, so a page lookup is a v_readlane instead
-      // of a global-memory round trip per page; refilled every 64 pages.
-      int bt_base = lo;
+      // Block-table entries of the split live in one VGPR, lane i holding
+      // entry bt_base + i, so a lookup is a v_readlane instead of a global-
+      // memory round trip per page; refilled when a slice leaves the window.
+      const int nent = (L + bs - 1) / bs;                // table entries of the sequence
+      int bt_base = lo * kPage / bs;
       int bt_vec = bt_this;
-      auto page_of = [&](int j) -> int {
-        if ((unsigned)(j - bt_base) >= 64u) {        // uniform; also on a re-run from lo
-          bt_base = j;
-          bt_vec = bt[min(j + lane, nblk - 1)];
+      auto block_of = [&](int k) -> int {                // table entry k (wave-uniform)
+        if ((unsigned)(k - bt_base) >= 64u) {        // also on a re-run from lo
+          bt_base = k;
+          bt_vec = bt[min(k + lane, nent - 1)];
         }
-        return __builtin_amdgcn_readlane(bt_vec, j - bt_base);
+        return __builtin_amdgcn_readlane(bt_vec, k - bt_base);
+      };
+      auto page_src = [&](int j) -> PageSrc {            // this wave's slice of page j
+        if (!kAnyBlock) return src_of(block_of(j), 16 * wave);
+        const int t = slice_tok(j);
+        return src_of(block_of(min(t / bs, nent - 1)), t % bs);
       };
       for (int pass = 0;; ++pass) {
         bool need = false;
         if (!have_first) {
-          if (kFp8) dma_page_fp8<kSplit>(src_of(page_of(lo)), bufs[cur], wave);
-          else dma_page_bf16<kSplit>(src_of(page_of(lo)), bufs[cur], wave);
+          if (kFp8) dma_page_fp8<kSplit>(page_src(lo), bufs[cur], wave);
+          else dma_page_bf16<kSplit>(page_src(lo), bufs[cur], wave);
         }
         have_first = false;
         for (int j = lo; j < hi; ++j) {
@@ -767,7 +789,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           }
           NextPage nx;
           nx.valid = j + 1 < hi || next_has_pages;
-          nx.src = src_of(j + 1 < hi ? page_of(j + 1) : next_pg);
+          nx.src = j + 1 < hi ? page_src(j + 1) : src_of(next_blk, 16 * wave % bs);
           nx.dst = bufs[cur ^ 1];
           nx.wave = wave;
           const LDS_AS uint8_t *pg = bufs[cur];
@@ -976,8 +998,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), smem, stream, a);
     return hipGetLastError();
   };
-  if (a.kv_fp8) return a.kv_rope ? launch(mla_decode_kernel<true, true>) : launch(mla_decode_kernel<true, false>);
-  return a.kv_rope ? launch(mla_decode_kernel<false, true>) : launch(mla_decode_kernel<false, false>);
+  auto by_block = [&](auto fp8, auto split) -> hipError_t {
+    constexpr bool f = decltype(fp8)::value, s = decltype(split)::value;
+    return a.page_size == kPage ? launch(mla_decode_kernel<f, s, false>) : launch(mla_decode_kernel<f, s, true>);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (a.kv_fp8) return a.kv_rope ? by_block(T{}, T{}) : by_block(T{}, F{});
+  return a.kv_rope ? by_block(F{}, T{}) : by_block(F{}, F{});
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {

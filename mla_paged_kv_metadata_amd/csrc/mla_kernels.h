@@ -14,7 +14,7 @@ constexpr int kMetaThreads = 256;
 
 struct DecodeArgs {
   const uint16_t *q;          // bf16 bits [B][s_q][Hq][q_stride]
-  const uint8_t *kv;          // [num_blocks][64][Hk][576 or 512] bf16 or e4m3fn
+  const uint8_t *kv;          // [num_blocks][page_size][Hk][576 or 512] bf16 or e4m3fn
   const int32_t *block_table; // [B][max_blocks]
   const int32_t *seqlens;     // [B]
   const int32_t *tile_md;     // [num_parts][8], one row per part
@@ -24,13 +24,14 @@ struct DecodeArgs {
   uint16_t *part_o;           // bf16 bits [slots][Hk][M][512], slots = batch + num_parts - 1
   float *part_lse;            // [slots][Hk][M]
   int batch, s_q, hq, hk, group, rows, max_blocks, row_tiles, num_parts, num_blocks;
+  int page_size;              // tokens per cache block, a multiple of 16
   int kv_fp8, causal;
   float scale_log2;           // softmax_scale * log2(e)
   float v_scale;
   int q_stride;               // elements per q row: 576, or 512 with q_rope
   const uint16_t *q_rope;     // nullptr, or bf16 bits [B][s_q][Hq][64]: the rope columns of q
-  const uint8_t *kv_rope;     // nullptr, or [num_blocks][64][Hk][64]: the rope columns of the cache
-                              // (kv then holds [num_blocks][64][Hk][512])
+  const uint8_t *kv_rope;     // nullptr, or [num_blocks][page_size][Hk][64]: the rope columns of the
+                              // cache (kv then holds [num_blocks][page_size][Hk][512])
   const float *sinks;         // nullptr, or fp32 [Hq] per-head sink logits
   const float *bmm1_dev;      // nullptr, or fp32 [1] replacing softmax_scale
   const float *bmm2_dev;      // nullptr, or fp32 [1] replacing v_scale

@@ -64,7 +64,7 @@ def _decode(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), 1), (dict(out=0), 1), (dict(lse=0), 1), (dict(batch=0), 1), (dict(hq=6, hk=4), 1),
     (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(scale=-0.5), 2), (dict(d=192), 2), (dict(dv=128), 2),
-    (dict(page=16), 2), (dict(dt=7), 2), (dict(s_q=9, hq=128), 2), (dict(batch=9000), 2),
+    (dict(page=24), 2), (dict(page=8), 2), (dict(page=0), 1), (dict(dt=7), 2), (dict(s_q=9, hq=128), 2), (dict(batch=9000), 2),
     (dict(wsb=16), 3), (dict(ws=0), 3),
 ])
 def test_decode_rejects_bad_arguments_before_any_device_call(kw, status):

@@ -12,7 +12,7 @@ import torch
 
 from oracle import (E4M3FN_TABLE, attend, bf16_bits_to_f64, decode_kv, fused_fp8_scales,
                     gather_rows, lse_merge, mla_decode, mla_decode_f64, visible_keys)
-from workloads import bf16_bits_from_f32, make_config, make_workload
+from workloads import bf16_bits_from_f32, make_config, make_workload, repage
 
 D, DV = 576, 512
 
@@ -371,3 +371,18 @@ def test_dominant_sink_silences_the_keys():
     o, l = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, sinks=np.full(8, 200.0))
     assert np.abs(o).max() < 1e-40
     assert np.allclose(l, 200.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("P", [16, 48, 128])
+def test_block_size_is_bitwise_invisible(kv_dtype, P):
+    """The same token rows in blocks of P tokens, with NaN in the rows past each
+    sequence's end, give bitwise the oracle's 64-token-block result."""
+    w = make_workload(seqlens=[0, 1, 17, 64, 65, 300, 129], num_heads_q=8, s_q=2, causal=True,
+                      kv_dtype=kv_dtype, seed=23)
+    r = repage(w, P, seed=4, pad="oob")
+    assert r.kv.shape[1] == P
+    s = 1 / 24
+    o1, l1 = mla_decode(w.q_bits, w.kv, kv_dtype, w.block_table, w.cache_seqlens, DV, s, True)
+    o2, l2 = mla_decode(r.q_bits, r.kv, kv_dtype, r.block_table, r.cache_seqlens, DV, s, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

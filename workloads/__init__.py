@@ -10,4 +10,5 @@ from .mla_inputs import (  # noqa: F401
     bf16_bits_from_f32,
     make_config,
     make_workload,
+    repage,
 )

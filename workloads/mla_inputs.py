@@ -85,7 +85,7 @@ class Workload:
     cache_seqlens: np.ndarray            # (B,) int32
     block_table: np.ndarray              # (B, max_blocks) int32
     q_bits: np.ndarray                   # (B, s_q, H, 576) uint16 (bf16 bits)
-    kv: np.ndarray                       # (num_blocks, 64, H_k, 576) uint16 bf16 bits or uint8 e4m3fn codes
+    kv: np.ndarray                       # (num_blocks, page_block_size, H_k, 576) bf16 bits or e4m3fn codes
     kv_dtype: str                        # "bf16" or "fp8_e4m3fn"
     causal: bool
     k_scale: float = 1.0                 # per-tensor dequant scale of the cache (fp8 only)
@@ -107,9 +107,9 @@ class Workload:
         return (L + self.page_block_size - 1) // self.page_block_size
 
 
-def _page_pool(rng, seqlens, num_heads_k, extra_pages=0, padding="zero"):
+def _page_pool(rng, seqlens, num_heads_k, extra_pages=0, padding="zero", page=PAGE):
     """Shuffled page pool: pages assigned b-major from one random permutation."""
-    nblk = [(int(L) + PAGE - 1) // PAGE for L in seqlens]
+    nblk = [(int(L) + page - 1) // page for L in seqlens]
     used = sum(nblk)
     num_blocks = max(1, used + extra_pages)
     perm = rng.permutation(num_blocks).astype(np.int32)
@@ -130,17 +130,19 @@ def _page_pool(rng, seqlens, num_heads_k, extra_pages=0, padding="zero"):
 def make_workload(*, name="custom", seqlens: Sequence[int], s_q=1, num_heads_q=16, num_heads_k=1,
                   causal=False, kv_dtype="bf16", seed=0, q_mul=1.0, extra_pages=0,
                   padding="zero", rng: Optional[np.random.Generator] = None,
-                  block_table: Optional[np.ndarray] = None, num_blocks: Optional[int] = None) -> Workload:
-    """General seeded workload.  Draw order: (lengths drawn by caller), permutation, q, cache."""
+                  block_table: Optional[np.ndarray] = None, num_blocks: Optional[int] = None,
+                  page_block_size: int = PAGE) -> Workload:
+    """General seeded workload.  Draw order: (lengths drawn by caller), permutation, q, cache.
+    page_block_size: tokens per cache block (64 unless a test asks for another)."""
     rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
     seqlens = np.asarray(seqlens, dtype=np.int32)
     B = int(seqlens.shape[0])
     if block_table is None:
-        bt, nb = _page_pool(rng, seqlens, num_heads_k, extra_pages, padding)
+        bt, nb = _page_pool(rng, seqlens, num_heads_k, extra_pages, padding, page_block_size)
     else:
         bt, nb = np.ascontiguousarray(block_table, dtype=np.int32), int(num_blocks)
     q = _normal_bf16(rng, B * s_q * num_heads_q * HEAD_DIM, q_mul).reshape(B, s_q, num_heads_q, HEAD_DIM)
-    nkv = nb * PAGE * num_heads_k * HEAD_DIM
+    nkv = nb * page_block_size * num_heads_k * HEAD_DIM
     k_scale = v_scale = 1.0
     if kv_dtype == "bf16":
         kv = _normal_bf16(rng, nkv)
@@ -149,10 +151,10 @@ def make_workload(*, name="custom", seqlens: Sequence[int], s_q=1, num_heads_q=1
         k_scale = v_scale = s            # K and V are the same cached rows
     else:
         raise ValueError(kv_dtype)
-    kv = kv.reshape(nb, PAGE, num_heads_k, HEAD_DIM)
+    kv = kv.reshape(nb, page_block_size, num_heads_k, HEAD_DIM)
     return Workload(name=name, batch=B, s_q=s_q, num_heads_q=num_heads_q, num_heads_k=num_heads_k,
                     cache_seqlens=seqlens, block_table=bt, q_bits=q, kv=kv, kv_dtype=kv_dtype,
-                    causal=causal, k_scale=k_scale, v_scale=v_scale)
+                    causal=causal, k_scale=k_scale, v_scale=v_scale, page_block_size=page_block_size)
 
 
 CONFIGS = {
@@ -195,3 +197,38 @@ def make_config(cfg: int, seed: Optional[int] = None, *, padding="zero", long_at
         return make_workload(name="c5_fp8", seqlens=seqlens, num_heads_q=128, kv_dtype="fp8_e4m3fn",
                              rng=rng, padding=padding)
     raise ValueError(f"unknown config {cfg}")
+
+
+def repage(w: Workload, page_block_size: int, seed: int = 0, pad: str = "nan") -> Workload:
+    """The same workload with its cache re-laid in blocks of page_block_size tokens.
+
+    Token t of sequence b keeps its row; the sequence's blocks come from a
+    fresh seeded permutation of the new pool.  Rows of a last block past the
+    sequence's end are filled per ``pad``: "nan" (bf16 0x7FC0 / e4m3fn 0x7F,
+    so that any use of them shows), or "oob" = table entries past a
+    sequence's blocks set to 0x7FFFFFF0 as well.
+    """
+    P = int(page_block_size)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nblk = [(int(L) + P - 1) // P for L in w.cache_seqlens]
+    nb = max(1, sum(nblk))
+    perm = rng.permutation(nb).astype(np.int32)
+    fill = 0x7FC0 if w.kv.dtype == np.uint16 else 0x7F
+    kv = np.full((nb, P) + w.kv.shape[2:], fill, dtype=w.kv.dtype)
+    bt = np.zeros((w.batch, max(1, max(nblk) if nblk else 1)), dtype=np.int32)
+    if pad == "oob":
+        bt[:] = 0x7FFFFFF0
+    old = w.page_block_size
+    o = 0
+    for b, n in enumerate(nblk):
+        L = int(w.cache_seqlens[b])
+        if L == 0:
+            continue
+        rows = np.concatenate([w.kv[w.block_table[b, j]] for j in range((L + old - 1) // old)])[:L]
+        for j in range(n):
+            blk = perm[o + j]
+            bt[b, j] = blk
+            seg = rows[j * P:(j + 1) * P]
+            kv[blk, :seg.shape[0]] = seg
+        o += n
+    return dataclasses.replace(w, name=f"{w.name}_ps{P}", block_table=bt, kv=kv, page_block_size=P)
