@@ -427,7 +427,7 @@ def main():
     dec_gbs = alg_bytes / dec_s / 1e9
     dec_tflops = flops / dec_s / 1e12
     # The shape's roofline: HBM bytes at 8 TB/s against bf16 MFMA flops at 2.5
-    # PFLOP/s (fp8 caches are widened to bf16, so bf16 is their MFMA peak too).
+    # PFLOP/s (fp8 codes become bf16 MFMA operands, so bf16 is their MFMA peak too).
     mfma_bound = flops / (BF16_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
