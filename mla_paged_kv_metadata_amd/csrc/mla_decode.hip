@@ -99,12 +99,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (wait_vmcnt) before the barrier that publishes a page.  M0 holds the LDS
 // base; an M0 write needs one wait state before an LDS-DMA instruction.  The
 // instruction's immediate offset applies to the global and the LDS address
-// alike, so M0 is lowered by it.
+// alike, so M0 is lowered by it.  Cache pages are read exactly once, so the
+// copy carries the non-temporal hint: the lines it brings into L2 go first,
+// and q rows and partial outputs (which are reused) stay resident longer.
 template <int kImm>
 __device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) {
   static_assert(kImm >= 0 && kImm < 4096, "global offset field");
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds) - kImm;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "s"(base),
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(src), "s"(base),
                "n"(kImm)
                : "m0");
 }
