@@ -693,16 +693,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   // table entry base + i, base = the entry of the split's first token.
   int bt_pref = 0;
   {
-    // The part's first block-table entries and length load together, and
-    // its q goes out while they are in flight; then its first page.  (Lanes
-    // past the split's blocks hold entries that are never used; the index is
-    // clamped into the table row.)
+    // The part's first block-table entries and length load together; then
+    // its first page's copy goes out, and then its q.  Every workgroup starts
+    // at once and the start-up loads share HBM, so the page is requested
+    // first: the wait before the first page then ends about 1 us earlier than
+    // with q first, although the q loads now start one table round trip
+    // later.  (Lanes past the split's blocks hold entries that are never
+    // used; the index is clamped into the table row.)
     const int first0 = max(0, md[1]);
     const int base0 = first0 * kPage / bs;
     const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
     bt_pref = bt0[min(base0 + lane, a.max_blocks - 1)];
     const int len0 = seq_len(b0);
-    load_q(b0);
     const int nblk0 = (len0 + kPage - 1) / kPage;
     const int hi0 = seq_end(b0, nblk0);
     if (hi0 > first0) {                               // then the split's first page is first0
@@ -715,6 +717,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
     }
+    load_q(b0);
   }
   for (int b = b0; b <= b1; ++b) {
     const int L = seq_len(b);
