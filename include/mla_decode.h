@@ -122,8 +122,9 @@ int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int heads_per_h
                         int num_parts, int fixed_cost, int32_t *tile_md, int32_t *num_splits, void *stream);
 
 /* Host only.  Bytes of split workspace mla_decode_fwd needs (bf16 partial
- * outputs and fp32 log-sum-exps of up to batch + num_parts - 1 splits),
- * written to *bytes.  Returns MLA_OK or INVALID_ARG. */
+ * outputs and fp32 log-sum-exps of up to batch + num_parts - 1 splits; the
+ * partial outputs of each KV head are kept in whole blocks of 32 rows), written
+ * to *bytes.  Returns MLA_OK or INVALID_ARG. */
 int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, int head_dim_v, int num_parts,
                         size_t *bytes);
 

@@ -64,6 +64,8 @@ int check_heads(int batch, int heads_per_head_k, int num_heads_k) {
 }
 
 int row_tiles(int rows) { return (rows + mla::kRowsPerTile - 1) / mla::kRowsPerTile; }
+// Partial outputs are stored in whole 32-row wave blocks.
+size_t rows_pad(size_t rows) { return (rows + mla::kPartRows - 1) / mla::kPartRows * mla::kPartRows; }
 
 // Per-split overhead in page units: a split loads its rows' q and writes its
 // output rows (or a partial) on top of its pages; on MI355X that measured
@@ -130,8 +132,9 @@ int mla_workspace_bytes(int batch, int s_q, int num_heads_q, int num_heads_k, in
     return fail(MLA_ERR_INVALID_ARG, "sizes must be >= 1");
   if (num_heads_q % num_heads_k) return fail(MLA_ERR_INVALID_ARG, "num_heads_q must be a multiple of num_heads_k");
   const size_t slots = (size_t)batch + (size_t)num_parts;
-  const size_t rows = (size_t)s_q * (num_heads_q / num_heads_k) * num_heads_k;
-  *bytes = align256(slots * rows * head_dim_v * sizeof(uint16_t)) + align256(slots * rows * sizeof(float));
+  const size_t rows = (size_t)s_q * (num_heads_q / num_heads_k);
+  *bytes = align256(slots * num_heads_k * rows_pad(rows) * head_dim_v * sizeof(uint16_t)) +
+           align256(slots * num_heads_k * rows * sizeof(float));
   return MLA_OK;
 }
 
@@ -168,7 +171,7 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   if (batch > MLA_MAX_BATCH) return fail(MLA_ERR_UNSUPPORTED, "batch exceeds MLA_MAX_BATCH");
   // Row indices of out and of the partial slots are 32-bit in the kernels.
   if ((long long)batch * s_q * num_heads_q >= (1LL << 31) ||
-      ((long long)batch + num_parts) * rows * num_heads_k >= (1LL << 31))
+      ((long long)batch + num_parts) * (long long)rows_pad(rows) * num_heads_k >= (1LL << 31))
     return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * num_heads_q or the partial slots exceed 2^31 rows");
   size_t need = 0;
   int rc = mla_workspace_bytes(batch, s_q, num_heads_q, num_heads_k, head_dim_v, num_parts, &need);
@@ -188,7 +191,8 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   a.lse = lse;
   const size_t slots = (size_t)batch + (size_t)num_parts;
   a.part_o = (uint16_t *)workspace;
-  a.part_lse = (float *)((char *)workspace + align256(slots * rows * num_heads_k * head_dim_v * sizeof(uint16_t)));
+  a.part_lse = (float *)((char *)workspace +
+                          align256(slots * rows_pad(rows) * num_heads_k * head_dim_v * sizeof(uint16_t)));
   a.batch = batch;
   a.s_q = s_q;
   a.hq = num_heads_q;

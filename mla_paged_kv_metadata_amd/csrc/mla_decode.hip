@@ -604,6 +604,30 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, 
   }
 }
 
+// Writes this wave's 32 x 512 split partial (times f, rounded to bf16) in
+// accumulator order: 16-byte chunk (2t + pp) * 64 + lane of the wave's 32 KiB
+// block holds o[t][8pp .. 8pp + 7] of that lane, i.e. row lane % 32, dims
+// 32t + 16pp + 4hl + {0..3} and 32t + 16pp + 8 + 4hl + {0..3} (hl = lane / 32).
+// Each store instruction then writes 1 KiB contiguous; the row-major form
+// above touches 32 rows per instruction, and on the standard B=64 decode the
+// last split's epilogue took about 4.1 us that way against 2.0 us this way.
+// Rows past the last real row of the block are written too (the workspace
+// holds whole 32-row blocks) and never read.
+__device__ __forceinline__ void store_acc_block(const f32x16 (&o)[kOTiles], float f, uint16_t *blk) {
+  uint16_t *p = blk + lane_id_here() * 8;
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);
+      const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
+      const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);
+      const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
+      *(u32x4 *)(p + (2 * t + pp) * 512) = u32x4{a0, a1, b0, b1};
+    }
+  }
+}
+
 // Bijection of [0, n): workgroup w runs on XCD w % 8 (the dispatcher's
 // round-robin); XCD x gets the x-th contiguous block of parts.
 constexpr int kXcds = 8;
@@ -851,8 +875,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       const float v_scale = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
-      store_rows(o, direct ? inv * v_scale : inv, direct ? a.out : a.part_o, direct ? orow : prow,
-                 max(0, min(32, uniform_here(a.rows) - wrow0)));
+      const int rows_pad = (a.rows + kPartRows - 1) / kPartRows * kPartRows;
+      if (direct)
+        store_rows(o, inv * v_scale, a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
+      else
+        store_acc_block(o, inv, a.part_o + ((long)(slot * a.hk + hk) * rows_pad + wrow0) * kHeadDimV);
       if (lane_id_here() < 32 && c.row < a.rows) {
         if (direct) a.lse[((long)b * a.hq + c.h) * a.s_q + c.qi] = lse_v;
         else a.part_lse[prow] = lse_v;
@@ -861,20 +888,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   }
 }
 
+// The combine works on units of one 32-row partial block and kSlots of its
+// 32 chunk slots (slot = 2t + pp, see store_acc_block): 32 / kSlots units per
+// block.  A lane owns one row (lane % 32) and, in each of its slots, 8 dims
+// of it, so the per-row weights are per-lane scalars and every load is a
+// contiguous 1 KiB per wave.
+constexpr int kBlockSlots = 2 * kOTiles;                  // 32 chunk slots per 32-row block
+
 // Running merge of splits 0..n-1 (kBatch per iteration, all their loads in
-// flight together; the running max rescales the sums) of one row into
+// flight together; the running max rescales the sums) of one unit into
 // (mu, Z, acc): sum_k e^(lse_k - mu) = Z and sum_k e^(lse_k - mu) O_k = acc.
-template <int kBatch>
-__device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po, long sstride, int n, float &mu,
-                                             float &Z, float (&acc)[8]) {
+//   pl: this lane's row lse of split 0; po: this lane's first chunk of the
+//   unit in split 0; lstride / ostride: elements between splits.
+template <int kBatch, int kSlots>
+__device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po, long lstride, long ostride, int n,
+                                             float &mu, float &Z, float (&acc)[kSlots][8]) {
   for (int k0 = 0; k0 < n; k0 += kBatch) {
     float lk[kBatch];
-    bf16x8 vk[kBatch];
+    bf16x8 vk[kBatch][kSlots];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int k = min(k0 + i, n - 1);               // past n: a repeat, weighted 0 below
-      lk[i] = pl[k * sstride];
-      vk[i] = *(const bf16x8 *)(po + k * sstride * kHeadDimV);
+      lk[i] = pl[k * lstride];
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j) vk[i][j] = *(const bf16x8 *)(po + k * ostride + j * 512);
     }
     float mb = mu;
 #pragma unroll
@@ -884,112 +921,143 @@ __device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po
     const float sc = __builtin_amdgcn_exp2f((mu - mb) * kLog2e);   // 0 while mu = -inf
     Z *= sc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= sc;
     mu = mb;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const float w = k0 + i < n ? __builtin_amdgcn_exp2f((lk[i] - mu) * kLog2e) : 0.f;
       Z += w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w * (float)vk[i][e];
+      for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] += w * (float)vk[i][j][e];
     }
   }
 }
 
 // Folds the state (mu2, Z2, acc2) into (mu, Z, acc) (both relative to their
 // own max; a state with mu = -inf is empty).
-__device__ __forceinline__ void fold_state(float &mu, float &Z, float (&acc)[8], float mu2, float Z2,
-                                           const float (&acc2)[8]) {
+template <int kSlots>
+__device__ __forceinline__ void fold_state(float &mu, float &Z, float (&acc)[kSlots][8], float mu2, float Z2,
+                                           const float (&acc2)[kSlots][8]) {
   const float mm = fmaxf(mu, mu2);
   if (mm == kNegInf) return;
   const float s1 = mu == kNegInf ? 0.f : __builtin_amdgcn_exp2f((mu - mm) * kLog2e);
   const float s2 = mu2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((mu2 - mm) * kLog2e);
   Z = Z * s1 + Z2 * s2;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = acc[e] * s1 + acc2[e] * s2;
+  for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] * s1 + acc2[j][e] * s2;
   mu = mm;
 }
 
 // Merge the split partials of every sequence with more than one split:
 // out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
-// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  8 dims per
-// lane, workgroups of 4 waves.  Two launch shapes, chosen on the host:
-//   - 4 rows per workgroup, one wave per row (batches with a few splits per
-//     sequence);
+// lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  Workgroups of
+// 4 waves; two launch shapes, chosen on the host:
+//   - 4 units of 4 slots per workgroup, one wave per unit (batches with a few
+//     splits per sequence);
 //   - when there are more than 4 parts per sequence, so that some sequence
-//     may be split many ways: one workgroup per (sequence, row).  A sequence
-//     with at most kCombineWide splits is merged by the first wave alone (the
-//     others exit at once); one with more spreads each row over the 4 waves --
+//     may be split many ways: one workgroup per unit of 1 slot.  A sequence with at
+//     most kCombineWide splits is merged by the first wave alone (the others
+//     exit at once); one with more spreads the splits over the 4 waves --
 //     wave q merges splits q, q + 4, ... and the first wave folds the four
-//     states from LDS -- so a row spread over hundreds of parts gets four
-//     waves' worth of loads in flight.  A sink logit z (FlashInfer
-// MLA page, sinks) is folded last as a state (z, 1, 0): one more term of
-// weight e^z and no value.
+//     states from LDS in wave order -- so a sequence spread over hundreds of
+//     parts gets four waves' worth of loads in flight.
+// A sink logit z (FlashInfer MLA page, sinks) is folded last as a state
+// (z, 1, 0): one more term of weight e^z and no value.
 constexpr int kCombineWays = 4;
 constexpr int kCombineWide = 8;
-__host__ __device__ inline bool combine_per_row(const DecodeArgs &a) { return a.num_parts > 4 * a.batch; }
+__host__ __device__ inline bool combine_per_unit(const DecodeArgs &a) { return a.num_parts > 4 * a.batch; }
+__host__ __device__ inline int combine_units(const DecodeArgs &a, int slots) {
+  return a.hk * ((a.rows + kPartRows - 1) / kPartRows) * (kBlockSlots / slots);
+}
+template <int kSlots>
 __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const DecodeArgs a) {
-  __shared__ float st_mu[kCombineWays], st_z[kCombineWays];
-  __shared__ __attribute__((aligned(16))) float st_acc[kCombineWays][64 * 8];
+  constexpr int kGroups = kBlockSlots / kSlots;       // units per 32-row block
+  constexpr bool kWideShape = kSlots == 1;            // one workgroup per unit
+  __shared__ float st_mu[kWideShape ? kCombineWays : 1][64], st_z[kWideShape ? kCombineWays : 1][64];
+  __shared__ __attribute__((aligned(16))) float st_acc[kWideShape ? kCombineWays : 1][kSlots * 8][64];
   const int b = blockIdx.y;
   const int nrows = a.batch + a.num_parts - 1;        // partial slots written by the decode kernel
   const int slot0 = max(0, min(a.num_splits[b], nrows));
   const int n = min(a.num_splits[b + 1] - slot0, nrows - slot0);
   if (n <= 1) return;                                 // workgroup-uniform
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int hk, row;
+  int unit;
   bool wide = false;                                  // workgroup-uniform
-  if (combine_per_row(a)) {
-    hk = blockIdx.x / a.rows;
-    row = blockIdx.x - hk * a.rows;
+  if (kWideShape) {
+    unit = blockIdx.x;
     wide = n > kCombineWide;
     if (!wide && wv != 0) return;
   } else {
-    const int groups = (a.rows + kCombineWays - 1) / kCombineWays;
-    hk = blockIdx.x / groups;
-    row = (blockIdx.x - hk * groups) * kCombineWays + wv;
+    unit = blockIdx.x * kCombineWays + wv;
   }
+  if (unit >= combine_units(a, kSlots)) return;               // wave-uniform (whole workgroups in the wide shape)
+  const int blocks = (a.rows + kPartRows - 1) / kPartRows;
+  const int g = unit % kGroups, blk = (unit / kGroups) % blocks, hk = unit / (kGroups * blocks);
+  const int rows_pad = blocks * kPartRows;
+  const int row = blk * kPartRows + (lane & 31);
+  const int rowc = min(row, a.rows - 1);
   const int way = wide ? wv : 0, ways = wide ? kCombineWays : 1;
-  const bool valid = row < a.rows;                    // wave-uniform
-  const long sstride = (long)a.hk * a.rows;
   float mu = kNegInf, Z = 0.f;
-  float acc[8] = {};
-  if (valid && way < n) {
-    const float *pl = a.part_lse + ((long)(slot0 + way) * a.hk + hk) * a.rows + row;
-    const uint16_t *po = a.part_o + (((long)(slot0 + way) * a.hk + hk) * a.rows + row) * kHeadDimV + lane * 8;
-    merge_splits<8>(pl, po, ways * sstride, (n - way + ways - 1) / ways, mu, Z, acc);
+  float acc[kSlots][8] = {};
+  if (way < n) {
+    const long lstride = (long)a.hk * a.rows;
+    const long ostride = (long)a.hk * rows_pad * kHeadDimV;
+    const float *pl = a.part_lse + ((long)(slot0 + way) * a.hk + hk) * a.rows + rowc;
+    const uint16_t *po = a.part_o + ((long)(slot0 + way) * a.hk + hk) * rows_pad * kHeadDimV +
+                         (long)blk * kPartRows * kHeadDimV + (g * kSlots * 64 + lane) * 8;
+    merge_splits<kWideShape ? 8 : 4>(pl, po, ways * lstride, ways * ostride, (n - way + ways - 1) / ways, mu, Z, acc);
   }
-  if (wide) {
-    if (lane == 0) {
-      st_mu[wv] = mu;
-      st_z[wv] = Z;
-    }
-    *(f32x4 *)&st_acc[wv][lane * 8] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4 *)&st_acc[wv][lane * 8 + 4] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  if (kWideShape && wide) {
+    st_mu[wv][lane] = mu;
+    st_z[wv][lane] = Z;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st_acc[wv][j * 8 + e][lane] = acc[j][e];
     __syncthreads();
     if (wv != 0) return;
 #pragma unroll
-    for (int j = 1; j < kCombineWays; ++j) {
-      const f32x4 lo = *(const f32x4 *)&st_acc[j][lane * 8];
-      const f32x4 hi = *(const f32x4 *)&st_acc[j][lane * 8 + 4];
-      const float accj[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      fold_state(mu, Z, acc, st_mu[j], st_z[j], accj);
+    for (int q = 1; q < kCombineWays; ++q) {
+      float accq[kSlots][8];
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accq[j][e] = st_acc[q][j * 8 + e][lane];
+      fold_state(mu, Z, acc, st_mu[q][lane], st_z[q][lane], accq);
     }
   }
-  if (!valid) return;
-  const int qi = row / a.group;
-  const int h = hk * a.group + (row - qi * a.group);
+  const int qi = rowc / a.group;
+  const int h = hk * a.group + (rowc - qi * a.group);
   if (a.sinks) {
-    const float zero[8] = {};
+    const float zero[kSlots][8] = {};
     fold_state(mu, Z, acc, a.sinks[h], 1.f, zero);
   }
   const float inv = Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
-  uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + lane * 8;
-  bf16x8 ov;
+  // Slot j of the unit is chunk slot 2t + pp = kSlots g + j: this lane
+  // holds dims 32t + 16pp + 4hl + {0..3} (acc[j][0..3]) and + 8 (acc[j][4..7]).
+  // v_permlane32_swap with lane ^ 32 forms whole 16-byte chunks: lanes < 32
+  // then hold dims 32t + 16pp + 8 .. +15, lanes >= 32 dims 32t + 16pp .. +7.
+  const int hl = lane >> 5;
+  uint16_t *orow = a.out + (((long)b * a.s_q + qi) * a.hq + h) * kHeadDimV + 8 * (1 - hl);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(acc[e] * inv);
-  *(bf16x8 *)orow = ov;
-  if (lane == 0) a.lse[((long)b * a.hq + h) * a.s_q + qi] = Z > 0.f ? mu + __logf(Z) : kNegInf;
+  for (int j = 0; j < kSlots; ++j) {
+    const int tp = g * kSlots + j, t = tp >> 1, pp = tp & 1;
+    const unsigned a0 = pack_bf16(acc[j][0] * inv, acc[j][1] * inv);
+    const unsigned a1 = pack_bf16(acc[j][2] * inv, acc[j][3] * inv);
+    const unsigned b0 = pack_bf16(acc[j][4] * inv, acc[j][5] * inv);
+    const unsigned b1 = pack_bf16(acc[j][6] * inv, acc[j][7] * inv);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+    if (row < a.rows) *(u32x4 *)(orow + 32 * t + 16 * pp) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  }
+  if (g == 0 && lane < 32 && row < a.rows)
+    a.lse[((long)b * a.hq + h) * a.s_q + qi] = Z > 0.f ? mu + __logf(Z) : kNegInf;
 }
 
 }  // namespace
@@ -1014,9 +1082,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  const dim3 grid(combine_per_row(a) ? a.hk * a.rows : a.hk * ((a.rows + kCombineWays - 1) / kCombineWays),
-                  a.batch);
-  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(kCombineWays * 64), 0, stream, a);
+  if (combine_per_unit(a)) {
+    hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(combine_units(a, 1), a.batch), dim3(kCombineWays * 64), 0, stream,
+                       a);
+  } else {
+    const int units = combine_units(a, 4);
+    hipLaunchKernelGGL(mla_combine_kernel<4>, dim3((units + kCombineWays - 1) / kCombineWays, a.batch),
+                       dim3(kCombineWays * 64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

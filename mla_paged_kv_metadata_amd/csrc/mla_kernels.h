@@ -10,6 +10,7 @@ constexpr int kHeadDim = 576;
 constexpr int kHeadDimV = 512;
 constexpr int kPage = 64;
 constexpr int kRowsPerTile = 128;     // rows (query heads x s_q) per decode workgroup
+constexpr int kPartRows = 32;         // rows per block of the partial outputs (one wave's rows)
 constexpr int kMetaThreads = 256;
 
 struct DecodeArgs {
@@ -21,7 +22,8 @@ struct DecodeArgs {
   const int32_t *num_splits;  // [B+1]
   uint16_t *out;              // bf16 bits [B][s_q][Hq][512]
   float *lse;                 // [B][Hq][s_q]
-  uint16_t *part_o;           // bf16 bits [slots][Hk][M][512], slots = batch + num_parts - 1
+  uint16_t *part_o;           // bf16 bits [slots][Hk][ceil(M/32)][32 x 512 in accumulator order],
+                              // slots = batch + num_parts - 1
   float *part_lse;            // [slots][Hk][M]
   int batch, s_q, hq, hk, group, rows, max_blocks, row_tiles, num_parts, num_blocks;
   int page_size;              // tokens per cache block, a multiple of 16
