@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--copies", type=int, default=4, help="KV pool replicas rotated across steps")
     ap.add_argument("--num-parts", type=int, default=None, help="override the scheduler's balancing target")
+    ap.add_argument("--fixed-cost", type=int, default=None,
+                    help="override the scheduler's per-split cost in pages (mla_get_metadata_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--sinks", action="store_true", help="per-head attention sinks (mla_decode_fwd_ext)")
@@ -318,7 +320,8 @@ def main():
 
     def step(i):
         kv = kvs[i % len(kvs)]
-        mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, tile_md=md, num_splits=ns)
+        mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, fixed_cost=args.fixed_cost, tile_md=md,
+                             num_splits=ns)
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
                            lse=lse, workspace=ws, stage="splits", **ext_for(i))
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2, causal=w.causal, out=out,
@@ -372,7 +375,8 @@ def main():
     # replayed like the steps, else eager), bracketed by HIP events on the
     # launch stream; the average launch of the decode kernel gives the roofline.
     def meta_call(i):
-        mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, tile_md=md, num_splits=ns)
+        mla.mla_get_metadata(sl, hpk, w.num_heads_k, num_parts=P, fixed_cost=args.fixed_cost, tile_md=md,
+                             num_splits=ns)
 
     def decode_call(i):
         mla.mla_decode_fwd(q, kvs[i % len(kvs)], bt, sl, 512, md, ns, softmax_scale=s1, v_scale=s2,
@@ -460,6 +464,7 @@ def main():
                                                     "bf16 q ~N(0,1), default scale",
                    "batch": w.batch, "seq_len_q": w.s_q, "num_heads_q": w.num_heads_q, "causal": bool(w.causal),
                    "kv_dtype": w.kv_dtype, "total_keys": int(w.cache_seqlens.sum()), "num_parts": P,
+                   **({"fixed_cost": args.fixed_cost} if args.fixed_cost else {}),
                    "kv_copies": len(kvs),
                    "inputs": "+".join(n for n, f in (("sinks", args.sinks), ("split_cache_q", args.split_cache),
                                                      ("device_scales", args.device_scales)) if f) or "plain"},
