@@ -43,6 +43,12 @@ def test_workspace_bytes():
     n = mla.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
     slots = 64 + 256
     assert n >= slots * 128 * 512 * 2 + slots * 128 * 4      # bf16 partial outputs, fp32 lse
+    # Partial outputs are kept in whole 32-row blocks per KV head: 20 rows take a block
+    # of 32, and 48 rows (s_q 3 x 16 heads) two blocks, for each of 2 KV heads.
+    n = mla.mla_workspace_bytes(2, 1, 20, 1, 512, 8)
+    assert n >= (2 + 8) * 32 * 512 * 2 + (2 + 8) * 20 * 4
+    n = mla.mla_workspace_bytes(3, 3, 32, 2, 512, 5)
+    assert n >= (3 + 5) * 2 * 64 * 512 * 2 + (3 + 5) * 2 * 48 * 4
     with pytest.raises(mla.MlaError) as e:
         mla.mla_workspace_bytes(0, 1, 128, 1, 512, 256)
     assert e.value.status == 1
