@@ -898,9 +898,11 @@ constexpr int kBlockSlots = 2 * kOTiles;                  // 32 chunk slots per 
 // Running merge of splits 0..n-1 (kBatch per iteration, all their loads in
 // flight together; the running max rescales the sums) of one unit into
 // (mu, Z, acc): sum_k e^(lse_k - mu) = Z and sum_k e^(lse_k - mu) O_k = acc.
+// Past the last split a batch either loads nothing (kGuard) or repeats the
+// last split's loads, weighted 0 (cheaper when a wave merges many splits).
 //   pl: this lane's row lse of split 0; po: this lane's first chunk of the
 //   unit in split 0; lstride / ostride: elements between splits.
-template <int kBatch, int kSlots>
+template <int kBatch, int kSlots, bool kGuard = false>
 __device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po, long lstride, long ostride, int n,
                                              float &mu, float &Z, float (&acc)[kSlots][8]) {
   for (int k0 = 0; k0 < n; k0 += kBatch) {
@@ -909,6 +911,12 @@ __device__ __forceinline__ void merge_splits(const float *pl, const uint16_t *po
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int k = min(k0 + i, n - 1);               // past n: a repeat, weighted 0 below
+      if (kGuard && k0 + i >= n) {                    // wave-uniform
+        lk[i] = kNegInf;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) vk[i][j] = bf16x8{};
+        continue;
+      }
       lk[i] = pl[k * lstride];
 #pragma unroll
       for (int j = 0; j < kSlots; ++j) vk[i][j] = *(const bf16x8 *)(po + k * ostride + j * 512);
@@ -957,11 +965,12 @@ __device__ __forceinline__ void fold_state(float &mu, float &Z, float (&acc)[kSl
 // Merge the split partials of every sequence with more than one split:
 // out = v_scale * sum_k w_k O_k / sum_k w_k, w_k = exp(lse_k - max lse),
 // lse = max + ln sum_k w_k.  Splits with lse = -inf weigh 0.  Workgroups of
-// 4 waves; two launch shapes, chosen on the host:
-//   - 4 units of 4 slots per workgroup, one wave per unit (batches with a few
-//     splits per sequence);
+// 4 waves and units of kCombineSlots slots; two launch shapes, chosen on the
+// host:
+//   - 4 units per workgroup, one wave per unit, 4 splits per round (batches
+//     with a few splits per sequence);
 //   - when there are more than 4 parts per sequence, so that some sequence
-//     may be split many ways: one workgroup per unit of 1 slot.  A sequence with at
+//     may be split many ways: one workgroup per unit.  A sequence with at
 //     most kCombineWide splits is merged by the first wave alone (the others
 //     exit at once); one with more spreads the splits over the 4 waves --
 //     wave q merges splits q, q + 4, ... and the first wave folds the four
@@ -971,14 +980,14 @@ __device__ __forceinline__ void fold_state(float &mu, float &Z, float (&acc)[kSl
 // (z, 1, 0): one more term of weight e^z and no value.
 constexpr int kCombineWays = 4;
 constexpr int kCombineWide = 8;
+constexpr int kCombineSlots = 1;                      // chunk slots per unit (1 KiB per split and wave)
 __host__ __device__ inline bool combine_per_unit(const DecodeArgs &a) { return a.num_parts > 4 * a.batch; }
 __host__ __device__ inline int combine_units(const DecodeArgs &a, int slots) {
   return a.hk * ((a.rows + kPartRows - 1) / kPartRows) * (kBlockSlots / slots);
 }
-template <int kSlots>
+template <int kSlots, bool kWideShape>
 __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const DecodeArgs a) {
   constexpr int kGroups = kBlockSlots / kSlots;       // units per 32-row block
-  constexpr bool kWideShape = kSlots == 1;            // one workgroup per unit
   __shared__ float st_mu[kWideShape ? kCombineWays : 1][64], st_z[kWideShape ? kCombineWays : 1][64];
   __shared__ __attribute__((aligned(16))) float st_acc[kWideShape ? kCombineWays : 1][kSlots * 8][64];
   const int b = blockIdx.y;
@@ -1011,7 +1020,7 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
     const float *pl = a.part_lse + ((long)(slot0 + way) * a.hk + hk) * a.rows + rowc;
     const uint16_t *po = a.part_o + ((long)(slot0 + way) * a.hk + hk) * rows_pad * kHeadDimV +
                          (long)blk * kPartRows * kHeadDimV + (g * kSlots * 64 + lane) * 8;
-    merge_splits<kWideShape ? 8 : 4>(pl, po, ways * lstride, ways * ostride, (n - way + ways - 1) / ways, mu, Z, acc);
+    merge_splits<kWideShape ? 8 : 4, kSlots, !kWideShape>(pl, po, ways * lstride, ways * ostride, (n - way + ways - 1) / ways, mu, Z, acc);
   }
   if (kWideShape && wide) {
     st_mu[wv][lane] = mu;
@@ -1082,14 +1091,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  if (combine_per_unit(a)) {
-    hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(combine_units(a, 1), a.batch), dim3(kCombineWays * 64), 0, stream,
-                       a);
-  } else {
-    const int units = combine_units(a, 4);
-    hipLaunchKernelGGL(mla_combine_kernel<4>, dim3((units + kCombineWays - 1) / kCombineWays, a.batch),
-                       dim3(kCombineWays * 64), 0, stream, a);
-  }
+  const int units = combine_units(a, kCombineSlots);
+  if (combine_per_unit(a))
+    hipLaunchKernelGGL((mla_combine_kernel<kCombineSlots, true>), dim3(units, a.batch), dim3(kCombineWays * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((mla_combine_kernel<kCombineSlots, false>), dim3((units + kCombineWays - 1) / kCombineWays,
+                       a.batch), dim3(kCombineWays * 64), 0, stream, a);
   return hipGetLastError();
 }
 
