@@ -171,10 +171,12 @@ def trace_summary(trace_dir, commands, bench_json=None):
     print(open(md).read())
 
 
-def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0):
+def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0, min_s=10.0):
     """The fp64 oracle on the host cores over as many whole sequences as fit the
     budget, timed; the GPU's outputs of the same sequences (out_np, lse_np, from
-    the last timed step) are checked against its results on the way."""
+    the last timed step) are checked against its results on the way.  When the
+    whole workload takes less than min_s, it is run again (whole passes) until
+    min_s of oracle time has accumulated, and the rate is taken over all passes."""
     from oracle import mla_decode as oracle_decode
     try:
         from threadpoolctl import threadpool_info
@@ -182,32 +184,37 @@ def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     sinks64 = None if sinks is None else sinks.astype(np.float64)
-    done, t_total, flops = [], 0.0, 0
+    done, t_total, flops, passes = [], 0.0, 0, 0
     d_out = d_lse = ref_max = 0.0
     L = w.cache_seqlens.astype(np.int64)
-    for b in range(w.batch):
-        t0 = time.perf_counter()
-        ro, rl = oracle_decode(w.q_bits, w.kv, w.kv_dtype, w.block_table, w.cache_seqlens, w.head_dim_v, scale,
-                               w.causal, vs, batches=[b], sinks=sinks64)
-        t_total += time.perf_counter() - t0
-        done.append(b)
-        n = sum(max(0, min(int(L[b]), int(L[b]) - w.s_q + 1 + i)) for i in range(w.s_q)) if w.causal \
-            else int(L[b]) * w.s_q
-        flops += 2 * w.num_heads_q * (w.head_dim + w.head_dim_v) * n
-        d_out = max(d_out, float(np.abs(out_np[b] - ro[b]).max()))
-        fin = np.isfinite(rl[b])
-        if fin.any():
-            d_lse = max(d_lse, float(np.abs(lse_np[b][fin] - rl[b][fin]).max()))
-        ref_max = max(ref_max, float(np.abs(ro[b]).max()))
-        if t_total >= budget_s:
+    while True:
+        for b in range(w.batch):
+            t0 = time.perf_counter()
+            ro, rl = oracle_decode(w.q_bits, w.kv, w.kv_dtype, w.block_table, w.cache_seqlens, w.head_dim_v, scale,
+                                   w.causal, vs, batches=[b], sinks=sinks64)
+            t_total += time.perf_counter() - t0
+            n = sum(max(0, min(int(L[b]), int(L[b]) - w.s_q + 1 + i)) for i in range(w.s_q)) if w.causal \
+                else int(L[b]) * w.s_q
+            flops += 2 * w.num_heads_q * (w.head_dim + w.head_dim_v) * n
+            if passes == 0:
+                done.append(b)
+                d_out = max(d_out, float(np.abs(out_np[b] - ro[b]).max()))
+                fin = np.isfinite(rl[b])
+                if fin.any():
+                    d_lse = max(d_lse, float(np.abs(lse_np[b][fin] - rl[b][fin]).max()))
+                ref_max = max(ref_max, float(np.abs(ro[b]).max()))
+            if t_total >= budget_s:
+                break
+        passes += 1
+        if t_total >= min_s or len(done) < w.batch:
             break
     coef = 5e-2 if w.kv_dtype == "fp8_e4m3fn" else 1e-2
     check = {"sequences": len(done), "max_abs_dout": d_out, "tol_out": coef * ref_max + 1e-3,
              "max_abs_dlse": d_lse, "tol_lse": 2e-3}
     check["pass"] = bool(d_out <= check["tol_out"] and d_lse <= check["tol_lse"])
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} sequences ({int(L[done].sum())} keys), fp64 NumPy, "
-                      f"{t_total:.2f} s"}, check
+            "sample": (f"{len(done)} of {w.batch} sequences ({int(L[done].sum())} keys)"
+                       + (f", {passes} passes" if passes > 1 else "") + f", fp64 NumPy, {t_total:.2f} s")}, check
 
 
 def main():
