@@ -138,6 +138,59 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, 
     print(open(md).read())
 
 
+def _per_dispatch_max(rows, counter, name_part):
+    """As _per_dispatch, but the largest instance value per dispatch (for the
+    GPU-wide GRBM counters, which every instance reports)."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", ""):
+            per[r["Dispatch_Id"]] = max(per.get(r["Dispatch_Id"], 0.0), float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"no {counter} rows for a kernel named *{name_part}*")
+    return sum(per.values()) / len(per), len(per)
+
+
+def mfma_summary(counter_dir, commands, simds=1024, xcds=8):
+    """Writes profiles/decode_c2_mfma_lds.md from one rocprofv3 --pmc run of the
+    matrix-core and LDS counters.  MFMA utilisation is the MFMA busy cycles per
+    SIMD over the GPU-active cycles of one XCD: GRBM_GUI_ACTIVE comes back as one
+    instance that adds up the 8 XCDs (its value / 8 matches the kernel's duration
+    times the shader clock)."""
+    rows = _counter_rows(counter_dir)
+    k = "mla_decode_kernel"
+    busy, n = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", k)
+    gui, _ = _per_dispatch_max(rows, "GRBM_GUI_ACTIVE", k)
+    mops, _ = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16", k)
+    conf, _ = _per_dispatch(rows, "SQ_LDS_BANK_CONFLICT", k)
+    lds_act, _ = _per_dispatch(rows, "SQ_LDS_IDX_ACTIVE", k)
+    lds_ins, _ = _per_dispatch(rows, "SQ_INSTS_LDS", k)
+    from workloads import make_config
+    w = make_config(2)
+    alg_flops, _, _ = work_counts(w)
+    util = 100.0 * (busy / simds) / (gui / xcds)
+    md = os.path.join(ROOT, "profiles", "decode_c2_mfma_lds.md")
+    with open(md, "w") as fh:
+        fh.write("# Matrix-core and LDS counters of mla_decode_kernel<bf16>, standard decode B=64 H=128 "
+                 "L~U[1024,4096]\n\n")
+        fh.write(f"rocprofv3 SQ/GRBM counters, averaged over {n} dispatches (one value per counter and "
+                 "dispatch as rocprofv3 reports it).\n\n")
+        fh.write("| quantity | value |\n|---|---|\n")
+        for name, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", gui),
+                        ("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), ("SQ_LDS_BANK_CONFLICT", conf),
+                        ("SQ_LDS_IDX_ACTIVE", lds_act), ("SQ_INSTS_LDS", lds_ins)):
+            fh.write(f"| {name} | {v:.0f} |\n")
+        fh.write(f"| MFMA busy cycles per SIMD (busy / {simds}) | {busy / simds:.0f} |\n")
+        fh.write(f"| GPU-active cycles per XCD (GRBM_GUI_ACTIVE / {xcds}) | {gui / xcds:.0f} |\n")
+        fh.write(f"| MFMA utilisation (per-SIMD busy / per-XCD active) | {util:.1f}% |\n")
+        fh.write(f"| bf16 MFMA FLOPs per dispatch (MOPS x 512) | {mops * 512 / 1e9:.2f} G |\n")
+        fh.write(f"| algorithmic FLOPs per dispatch | {alg_flops / 1e9:.2f} G |\n")
+        fh.write(f"| LDS bank-conflict cycles / LDS active cycles | {conf / max(lds_act, 1):.3f} |\n")
+        fh.write("\nCommands (from the repository root):\n\n")
+        for c in commands:
+            fh.write(f"    {c}\n")
+    print(open(md).read())
+
+
 def trace_summary(trace_dir, commands, bench_json=None):
     """Writes profiles/decode_c2_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder
     (and, if given, the JSON line that the profiled bench run printed)."""
@@ -241,6 +294,8 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise four rocprofv3 --pmc output folders into profiles/ (no GPU work)")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy for --pmc-summary")
+    ap.add_argument("--mfma-summary", metavar="COUNTER_DIR",
+                    help="write profiles/decode_c2_mfma_lds.md from a rocprofv3 --pmc run of the MFMA/LDS counters")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats folder into profiles/ (no GPU work)")
     ap.add_argument("--bench-json", help="the profiled run's JSON line, quoted in a --trace-summary file")
@@ -249,6 +304,9 @@ def main():
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, args.copy_mib, args.pmc_command)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, args.pmc_command)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.pmc_command, args.bench_json)
