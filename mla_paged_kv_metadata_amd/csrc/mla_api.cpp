@@ -68,9 +68,12 @@ int row_tiles(int rows) { return (rows + mla::kRowsPerTile - 1) / mla::kRowsPerT
 size_t rows_pad(size_t rows) { return (rows + mla::kPartRows - 1) / mla::kPartRows * mla::kPartRows; }
 
 // Per-split overhead in page units: a split loads its rows' q and writes its
-// output rows (or a partial) on top of its pages; on MI355X that measured
-// about four bf16 pages for a 128-row tile and shrinks with fewer rows.
-int default_fixed_cost(int rows) { return std::max(1, std::min(rows, mla::kRowsPerTile) / 32); }
+// output rows (or a partial) on top of its pages, and waits for its first
+// page.  On MI355X that measured about four bf16 pages for a 128-row tile;
+// with fewer rows the q and output traffic shrinks but the first page's wait
+// does not, and sweeps put the best value for a 16-row tile at 2-3 pages
+// (1 page was 10% slower on the skewed 16-head decode).
+int default_fixed_cost(int rows) { return std::max(2, std::min(rows, mla::kRowsPerTile) / 32); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
