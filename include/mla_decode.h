@@ -115,9 +115,10 @@ int mla_get_metadata(const int32_t *cache_seqlens, int batch, int heads_per_head
 
 /* As mla_get_metadata with an explicit per-split overhead `fixed_cost`
  * (in page units, >= 1) of the balancing cost model.  Sequence b costs
- * fixed_cost + ceil(L_b / 64) units; units are laid end to end in batch
- * order and cut into num_parts equal ranges of W = ceil(total / num_parts)
- * units. */
+ * fixed_cost + ceil(L_b / 64) units: ceil(fixed_cost / 2) overhead units,
+ * one unit per 64-token page, then the other floor(fixed_cost / 2) overhead
+ * units; units are laid end to end in batch order and cut into num_parts
+ * equal ranges of at most W = ceil(total / num_parts) units. */
 int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int heads_per_head_k, int num_heads_k,
                         int num_parts, int fixed_cost, int32_t *tile_md, int32_t *num_splits, void *stream);
 

@@ -4,7 +4,10 @@
 // outputs' shapes -- a (num_sm_parts, TileSchedulerMetaDataSize) int32 table
 // and num_splits (batch + 1) int32, "splits per sample" -- but not their
 // content.  The balancing rule is this library's own:
-//   sequence b costs fixed_cost + nblk_b units (nblk_b = ceil(L_b / 64));
+//   sequence b costs fixed_cost + nblk_b units (nblk_b = ceil(L_b / 64)):
+//   ceil(fixed_cost / 2) overhead units, its page units, then the other
+//   floor(fixed_cost / 2) overhead units (a split's overhead is both its q
+//   load at the start and its result stores at the end);
 //   units of all sequences are laid end to end in batch order; part p owns
 //   units [floor(p*total/P), floor((p+1)*total/P)) (P = num_parts), so parts
 //   differ by at most one unit and none idles while total >= P.  Part p works on
@@ -81,6 +84,7 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
                                           long long *pref, long long *cnt, long long *tmp) {
   const int tid = threadIdx.x;
   const T fc = fixed_cost;
+  const T fs = (fc + 1) / 2;                                  // overhead units before a sequence's pages
   const T total = (T)pref[B];
   const T P = num_parts;
   const T W = max((T)1, (total + P - 1) / P);                 // most units of one part
@@ -89,7 +93,7 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
 
   for (int b = tid; b < B; b += kT) {
     const T nblk = (T)(pref[b + 1] - pref[b]) - fc;
-    const T s = (T)pref[b] + fc;                            // first page unit of b
+    const T s = (T)pref[b] + fs;                            // first page unit of b
     cnt[b] = nblk <= 0 ? 1 : (total >= P ? part_of(s + nblk - 1) - part_of(s) + 1 : nblk);
   }
   __syncthreads();
@@ -100,7 +104,7 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
     int32_t *row = tile_md + (size_t)p * 8;
     const T u0 = bound(p), u1 = bound(p + 1);
     auto works = [&](int b) -> bool {
-      const T nblk = (T)(pref[b + 1] - pref[b]) - fc, s = (T)pref[b] + fc;
+      const T nblk = (T)(pref[b + 1] - pref[b]) - fc, s = (T)pref[b] + fs;
       if (nblk > 0) return s < u1 && s + nblk > u0;
       return u0 <= (T)pref[b] && (T)pref[b] < u1;
     };
@@ -119,8 +123,8 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
       row[0] = -1; row[1] = 0; row[2] = -1; row[3] = 0; row[4] = 0; row[7] = 0;
       continue;
     }
-    const T n0 = (T)(pref[b0 + 1] - pref[b0]) - fc, s0 = (T)pref[b0] + fc;
-    const T n1 = (T)(pref[b1 + 1] - pref[b1]) - fc, s1 = (T)pref[b1] + fc;
+    const T n0 = (T)(pref[b0 + 1] - pref[b0]) - fc, s0 = (T)pref[b0] + fs;
+    const T n1 = (T)(pref[b1 + 1] - pref[b1]) - fc, s1 = (T)pref[b1] + fs;
     T k0 = 0;
     if (n0 > 0) k0 = total >= P ? p - part_of(s0) : max(u0, s0) - s0;
     row[0] = b0;

@@ -6,9 +6,12 @@ scheduler" and num_splits of shape (batch + 1,) -- "splits per sample".  The
 rule below is this repository's own, written here as a plain walk over cost
 units so the GPU scheduler kernel can be compared with it bit for bit:
 
-  * Sequence b costs ``fixed_cost`` overhead units followed by one unit per
-    page, nblk_b = ceil(L_b / page).  Units of all sequences are laid end to end
-    in batch order; total = sum_b (fixed_cost + nblk_b).
+  * Sequence b costs ``fixed_cost`` overhead units and one unit per page,
+    nblk_b = ceil(L_b / page), laid out as ceil(fixed_cost / 2) overhead
+    units, the page units, then the other floor(fixed_cost / 2) overhead units
+    (a split's overhead is its q load at the start and its result stores at
+    the end).  Units of all sequences are laid end to end in batch order;
+    total = sum_b (fixed_cost + nblk_b).
   * Part p owns units [floor(p * total / num_parts), floor((p+1) * total /
     num_parts)): parts differ by at most one unit and none is left idle
     while total >= num_parts.  W = ceil(total / num_parts) is the most units
@@ -42,9 +45,11 @@ def schedule(cache_seqlens, num_parts: int, fixed_cost: int, page: int = 64):
         raise ValueError("need num_parts >= 1, fixed_cost >= 1, batch >= 1")
     nblk = [-(-x // page) for x in L]
     units = []                                   # (b, page index or -1 for overhead)
+    lead = (fixed_cost + 1) // 2
     for b in range(B):
-        units += [(b, -1)] * fixed_cost
+        units += [(b, -1)] * lead
         units += [(b, j) for j in range(nblk[b])]
+        units += [(b, -1)] * (fixed_cost - lead)
     total = len(units)
     W = max(1, -(-total // num_parts))
     bounds = [p * total // num_parts for p in range(num_parts + 1)]

@@ -73,6 +73,30 @@ def test_hand_worked_two_part_table():
     assert [r[0] for r in md.tolist()] == [-1, -1, -1, -1, 0]
 
 
+def test_hand_worked_overhead_before_and_after_pages():
+    # fixed_cost 2: one overhead unit before a sequence's pages and one after.
+    # Units: b0 = [o, p0, p1, o], b1 = [o, p0, p1, p2, p3, o]; total 10.
+    # Two parts (boundaries 0, 5, 10): part 0 owns b0 whole and b1's leading
+    # unit (no page of b1); part 1 owns b1's pages and its trailing unit.
+    md, ns = schedule([128, 256], 2, 2)
+    assert ns.tolist() == [0, 1, 2]
+    assert md.tolist() == [[0, 0, 0, 2, 0, 5, 2, 1], [1, 0, 1, 4, 0, 5, 2, 1]]
+    # Three parts (boundaries 0, 3, 6, 10; W = 4): part 0 = b0's leading unit
+    # and pages; part 1 = b0's trailing unit, b1's leading unit and page 0;
+    # part 2 = b1's pages 1-3 and trailing unit.  b1 has two splits.
+    md, ns = schedule([128, 256], 3, 2)
+    assert ns.tolist() == [0, 1, 3]
+    assert md.tolist() == [[0, 0, 0, 2, 0, 4, 2, 1], [1, 0, 1, 1, 0, 4, 2, 1], [1, 1, 1, 4, 1, 4, 2, 1]]
+
+
+def test_uniform_lengths_split_evenly():
+    # 128 sequences of 128 pages over 256 parts: with the overhead on both
+    # sides of the pages every part gets exactly 64 pages.
+    md, ns = schedule([8192] * 128, 256, 4)
+    pages = [hi - lo for _, _, _, lo, hi in expand_splits(md, [8192] * 128)]
+    assert len(pages) == 256 and set(pages) == {64}
+
+
 def test_long_sequence_is_spread_over_many_parts():
     L = make_config(4).cache_seqlens
     md, ns = schedule(L, 256, 2)
