@@ -102,13 +102,48 @@ __device__ __forceinline__ void wait_vmcnt() {
 // alike, so M0 is lowered by it.  Cache pages are read exactly once, so the
 // copy carries the non-temporal hint: the lines it brings into L2 go first,
 // and q rows and partial outputs (which are reused) stay resident longer.
-template <int kImm>
+template <int kImm, bool kNt = true>
 __device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) {
   static_assert(kImm >= 0 && kImm < 4096, "global offset field");
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds) - kImm;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(src), "s"(base),
-               "n"(kImm)
-               : "m0");
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(src),
+                 "s"(base), "n"(kImm)
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "s"(base),
+                 "n"(kImm)
+                 : "m0");
+}
+
+// q rows of a wave staged through LDS: the wave's 32 consecutive q rows
+// (32 x 1152 B, contiguous in memory) are copied as 36 LDS-DMA instructions
+// of 8 whole rows x 128 B each -- 8 cache lines per instruction, where the
+// direct fragment loads touch 32 rows per instruction -- into a 36 KiB LDS
+// region, then read back as the 36 MFMA B fragments.  Instruction i = 9R + c
+// covers rows 8R .. 8R+7 and 16-byte chunks 8c .. 8c+7; lane 8r + j fetches
+// chunk 8c + (j ^ qsw(r, R)) of row 8R + r, so that chunk C of row n sits at
+// byte 1024 (9 (n / 8) + C / 8) + 16 (8 (n % 8) + ((C % 8) ^ qsw(n % 8, n / 8))).
+// For one fragment (a fixed chunk) 16 consecutive rows then fall on 16
+// distinct 16-byte bank slots: the slot is 8 (n % 2) + ((C % 8) ^ qsw), and
+// qsw takes 8 distinct values over the rows of one parity.
+__device__ __forceinline__ int qsw(int r, int R) { return (r >> 1) | ((R & 1) << 2); }
+__device__ __forceinline__ void stage_q_rows(const uint8_t *qblock, LDS_AS uint8_t *region, int lane) {
+  const int r = lane >> 3, j = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 36; ++i) {
+    const int R = i / 9, c = i % 9;
+    lds_dma16<0, false>(qblock + (8 * R + r) * 1152 + 16 * (8 * c + (j ^ qsw(r, R))), region + 1024 * i);
+  }
+}
+__device__ __forceinline__ void read_q_rows(const LDS_AS uint8_t *region, int lane, bf16x8 (&qf)[36]) {
+  const int n = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) {
+    const int C = 2 * ks + hl;
+    qf[ks] = *(const LDS_AS bf16x8 *)(region + 1024 * (9 * (n >> 3) + (C >> 3)) +
+                                       16 * (8 * (n & 7) + ((C & 7) ^ qsw(n & 7, n >> 3))));
+  }
 }
 
 // HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above,
@@ -720,13 +755,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   // table entry base + i, base = the entry of the split's first token.
   int bt_pref = 0;
   {
-    // The part's first block-table entries and length load together; then
-    // its first page's copy goes out, and then its q.  Every workgroup starts
-    // at once and the start-up loads share HBM, so the page is requested
-    // first: the wait before the first page then ends about 1 us earlier than
-    // with q first, although the q loads now start one table round trip
-    // later.  (Lanes past the split's blocks hold entries that are never
-    // used; the index is clamped into the table row.)
+    // The part's first block-table entries and length load together.  Then
+    // either (a) its q rows are staged through LDS (stage_q_rows) and, once
+    // every wave has read them back, its first page's copy goes out; or (b)
+    // where the rows cannot be staged (split q, heads per KV head not a
+    // multiple of 32, a partial 128-row tile, no first page) the page's copy
+    // goes out first and then the direct q loads.  Every workgroup starts at
+    // once and the start-up loads share HBM; the direct q loads touch 32 rows
+    // per instruction and were the slower half of the start-up: on the
+    // standard B=64 decode (a) took the decode from 62.8 to 61.5 us, and in
+    // (b) requesting the page before q gained about 1 us over q first.
+    // (Lanes past the split's blocks hold entries that are never used; the
+    // index is clamped into the table row.)
     const int first0 = max(0, md[1]);
     const int base0 = first0 * kPage / bs;
     const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
@@ -734,6 +774,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int len0 = seq_len(b0);
     const int nblk0 = (len0 + kPage - 1) / kPage;
     const int hi0 = seq_end(b0, nblk0);
+    // (a): the tile's 4 x 32 rows are whole 32-row runs of consecutive q rows
+    // (no split q), and their 4 x 36 KiB fill both page buffers exactly.
+    const bool staged = a.q_rope == nullptr && a.group % 32 == 0 && (rt + 1) * kRowsPerTile <= a.rows &&
+                        a.q_stride == kHeadDim && hi0 > first0;   // workgroup-uniform
+    if (staged) {
+      const int qi = wrow0 / a.group, h0 = hk * a.group + wrow0 % a.group;
+      const uint8_t *qblock = (const uint8_t *)(a.q + (((long)b0 * a.s_q + qi) * a.hq + h0) * kHeadDim);
+      LDS_AS uint8_t *region = smem + wave * 32 * kHeadDim * 2;
+      stage_q_rows(qblock, region, lane);
+      wait_vmcnt<0>();
+      read_q_rows(region, lane, qf);
+      __syncthreads();                                // q read back before the page lands on it
+    }
     if (hi0 > first0) {                               // then the split's first page is first0
       // (A slice past the sequence's end takes its last block: its rows are
       // masked, and table entries past the sequence are never used.)
@@ -744,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
     }
-    load_q(b0);
+    if (!staged) load_q(b0);
   }
   for (int b = b0; b <= b1; ++b) {
     const int L = seq_len(b);
