@@ -59,6 +59,9 @@ extern "C" {
 #define MLA_MAX_BATCH 8192
 /* Largest rows per KV head (s_q * num_heads_q / num_heads_k). */
 #define MLA_MAX_ROWS 1024
+/* Bytes of the library's static device scratch used by mla_decode_fwd_noalloc
+ * (128 MiB per GPU, held until the process ends). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 enum mla_status {
   MLA_OK = 0,
@@ -245,6 +248,25 @@ int mla_decode_fwd_ext(const void *q, int batch, int s_q, int num_heads_q, int h
                        const int32_t *tile_md, int num_parts, const int32_t *num_splits,
                        void *workspace, size_t workspace_bytes,
                        void *out, float *lse, void *stream, const mla_decode_ext *ext);
+
+/* mla_decode_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, validation and results as mla_decode_fwd, without the
+ * workspace: the split partials live in a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on.
+ * The caller still passes every input and output.  A problem whose
+ * mla_workspace_bytes(...) exceeds MLA_NOALLOC_SCRATCH_BYTES is rejected with
+ * MLA_ERR_WORKSPACE_TOO_SMALL before any device call.  No call allocates or
+ * frees memory; the first call on a device looks up the array's address there
+ * (hipGetSymbolAddress) and keeps it.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (concurrent streams or
+ * threads) race and must be serialised by the caller. */
+int mla_decode_fwd_noalloc(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                           const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                           const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                           int head_dim_v, float softmax_scale, float v_scale, int causal,
+                           const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                           void *out, float *lse, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
 TILE_MD_INTS = 8
 HEAD_DIM = 576
 HEAD_DIM_V = 512
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 PAGE_BLOCK_SIZE = 64        # tokens per scheduling page (and the usual cache block)
 PAGE_BLOCK_ALIGN = 16       # a cache's page_block_size must be a multiple of this
 KV_BF16 = 0
@@ -58,6 +59,8 @@ def load_library(path: Optional[str] = None):
         fn.argtypes = _DECODE_ARGTYPES
     lib.mla_decode_fwd_ext.restype = _c_int
     lib.mla_decode_fwd_ext.argtypes = _DECODE_ARGTYPES + [ctypes.POINTER(DecodeExt)]
+    lib.mla_decode_fwd_noalloc.restype = _c_int
+    lib.mla_decode_fwd_noalloc.argtypes = _DECODE_ARGTYPES[:20] + _DECODE_ARGTYPES[22:]
     _lib = lib
     return lib
 
@@ -295,6 +298,42 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
     return out, lse
 
 
+def mla_decode_fwd_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                           cache_seqlens: torch.Tensor, head_dim_v: int, tile_scheduler_metadata: torch.Tensor,
+                           num_splits: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                           softmax_scale: Optional[float] = None, causal: bool = False,
+                           v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_fwd without a workspace (the library's static device scratch
+    holds the split partials); the caller provides out and lse.  Calls that
+    overlap in time on one GPU share that scratch and must not overlap."""
+    lib = load_library()
+    if softmax_scale is None:
+        softmax_scale = HEAD_DIM ** (-0.5)
+    dev = q.device
+    for t, name, dt in ((q, "q", torch.bfloat16), (kv_cache, "kv_cache", None), (block_table, "block_table", torch.int32),
+                        (cache_seqlens, "cache_seqlens", torch.int32),
+                        (tile_scheduler_metadata, "tile_scheduler_metadata", torch.int32),
+                        (num_splits, "num_splits", torch.int32), (out, "out", torch.bfloat16),
+                        (lse, "lse", torch.float32)):
+        _need(t, name, dt, dev)
+    B, s_q, Hq, D = q.shape
+    nb, page, hk, _, code = _kv_layout(kv_cache)
+    if tuple(out.shape) != (B, s_q, Hq, head_dim_v) or tuple(lse.shape) != (B, Hq, s_q):
+        raise ValueError("out must be (B, s_q, H_q, head_dim_v) and lse (B, H_q, s_q)")
+    if block_table.dim() != 2 or block_table.shape[0] != B or cache_seqlens.shape != (B,) \
+            or num_splits.shape != (B + 1,) or tile_scheduler_metadata.dim() != 2 \
+            or tile_scheduler_metadata.shape[1] != TILE_MD_INTS:
+        raise ValueError("block_table, cache_seqlens, tile_scheduler_metadata or num_splits has the wrong shape")
+    with torch.cuda.device(dev):
+        rc = lib.mla_decode_fwd_noalloc(
+            _ptr(q), B, s_q, Hq, D, _ptr(kv_cache), code, nb, page, hk, _ptr(block_table), block_table.shape[1],
+            _ptr(cache_seqlens), head_dim_v, float(softmax_scale), float(v_scale), int(bool(causal)),
+            _ptr(tile_scheduler_metadata), tile_scheduler_metadata.shape[0], _ptr(num_splits), _ptr(out), _ptr(lse),
+            _stream(dev))
+    _check(rc)
+    return out, lse
+
+
 def fp8_fused_scales(q_scale=1.0, k_scale=1.0, v_scale=1.0, o_scale=1.0, sm_scale=1.0, head_dim_qk=HEAD_DIM):
     """(bmm1_scale, bmm2_scale) as the FlashInfer MLA page fuses them."""
     return q_scale * k_scale * sm_scale / math.sqrt(head_dim_qk), v_scale * o_scale
@@ -311,4 +350,5 @@ def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v, t
 
 
 __all__ = ["load_library", "mla_num_parts", "mla_get_metadata", "mla_workspace_bytes", "mla_decode_fwd",
+           "mla_decode_fwd_noalloc",
            "get_mla_metadata", "flash_mla_with_kvcache", "fp8_fused_scales", "MlaError", "LIB_PATH"]

@@ -86,7 +86,7 @@ const char *mla_status_str(int status) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARG: return g_reason[0] ? g_reason : "invalid argument";
     case MLA_ERR_UNSUPPORTED: return g_reason[0] ? g_reason : "unsupported";
-    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_workspace_bytes()";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return g_reason[0] ? g_reason : "workspace smaller than mla_workspace_bytes()";
     case MLA_ERR_NO_DEVICE: return "no HIP device is visible";
     case MLA_ERR_HIP: return g_reason[0] ? g_reason : "HIP runtime error";
     default: return "unknown status";
@@ -179,7 +179,8 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   size_t need = 0;
   int rc = mla_workspace_bytes(batch, s_q, num_heads_q, num_heads_k, head_dim_v, num_parts, &need);
   if (rc) return rc;
-  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than mla_workspace_bytes()");
   DeviceInfo d;
   if ((rc = current_device(&d))) return rc;
 
@@ -291,6 +292,30 @@ int mla_decode_fwd_ext(const void *q, int batch, int s_q, int num_heads_q, int h
   return decode_call(stage, q, batch, s_q, num_heads_q, head_dim, kv_cache, kv_dtype, num_blocks, page_block_size,
                      num_heads_k, block_table, max_blocks_per_seq, cache_seqlens, head_dim_v, softmax_scale, v_scale,
                      causal, tile_md, num_parts, num_splits, workspace, workspace_bytes, out, lse, stream, ext);
+}
+
+int mla_decode_fwd_noalloc(const void *q, int batch, int s_q, int num_heads_q, int head_dim,
+                           const void *kv_cache, int kv_dtype, int num_blocks, int page_block_size, int num_heads_k,
+                           const int32_t *block_table, int max_blocks_per_seq, const int32_t *cache_seqlens,
+                           int head_dim_v, float softmax_scale, float v_scale, int causal,
+                           const int32_t *tile_md, int num_parts, const int32_t *num_splits,
+                           void *out, float *lse, void *stream) {
+  // The size check comes first, so an oversized request is refused before
+  // any device call.
+  size_t need = 0;
+  int rc = mla_workspace_bytes(batch, s_q, num_heads_q, num_heads_k, head_dim_v, num_parts, &need);
+  if (rc) return rc;
+  if (need > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "the problem's split workspace exceeds the static scratch (MLA_NOALLOC_SCRATCH_BYTES)");
+  DeviceInfo d;
+  if ((rc = current_device(&d))) return rc;
+  void *ws = nullptr;
+  hipError_t e = mla::noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, hipGetErrorString(e));
+  return decode_call(3, q, batch, s_q, num_heads_q, head_dim, kv_cache, kv_dtype, num_blocks, page_block_size,
+                     num_heads_k, block_table, max_blocks_per_seq, cache_seqlens, head_dim_v, softmax_scale, v_scale,
+                     causal, tile_md, num_parts, num_splits, ws, MLA_NOALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
 }  // extern "C"

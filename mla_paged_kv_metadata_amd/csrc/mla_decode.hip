@@ -38,7 +38,10 @@
 //    The fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
 //    softmax_scale and v_scale.
 #include "mla_kernels.h"
+#include <mutex>
 #include <type_traits>
+
+#include "../../include/mla_decode.h"
 
 namespace mla {
 namespace {
@@ -1155,6 +1158,35 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((mla_combine_kernel<kCombineSlots, false>), dim3((units + kCombineWays - 1) / kCombineWays,
                        a.batch), dim3(kCombineWays * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+// Device-resident scratch of the no-allocation entry point
+// (mla_decode_fwd_noalloc): the partial outputs and log-sum-exps that
+// mla_decode_fwd keeps in its caller's workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code the array's
+// name is only a stand-in for a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mla

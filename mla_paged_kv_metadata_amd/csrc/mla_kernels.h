@@ -43,5 +43,8 @@ hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int
                            int32_t *tile_md, int32_t *num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+// Device address of the static scratch array on the current device (looked
+// up once per device).
+hipError_t noalloc_scratch(void **ptr);
 
 }  // namespace mla

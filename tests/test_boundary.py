@@ -150,3 +150,19 @@ def test_python_wrapper_checks_split_layout_shapes():
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, kv_rope=torch.zeros((2, 64, 1, 32), dtype=torch.bfloat16))
     with pytest.raises(ValueError):      # q_rope with a 576-wide q
         mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, q_rope=torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16))
+
+
+def test_noalloc_refuses_oversized_problems_before_any_device_call():
+    # mla_workspace_bytes for 4096 sequences x 1024 rows is far above the
+    # static scratch; the call must fail before touching a device (dummy pointers).
+    lib = mla.load_library()
+    P = ctypes.c_void_p
+    rc = lib.mla_decode_fwd_noalloc(P(1), 4096, 8, 128, 576, P(1), 0, 8, 64, 1, P(1), 1, P(1), 512, 0.04, 1.0, 0,
+                                    P(1), 256, P(1), P(1), P(1), P(0))
+    assert rc == 3
+    assert b"scratch" in lib.mla_status_str(rc)
+    n = mla.mla_workspace_bytes(4096, 8, 128, 1, 512, 256)
+    assert n > mla.NOALLOC_SCRATCH_BYTES
+    # Invalid sizes are INVALID_ARG, as for mla_decode_fwd.
+    assert lib.mla_decode_fwd_noalloc(P(1), 0, 1, 16, 576, P(1), 0, 8, 64, 1, P(1), 1, P(1), 512, 0.04, 1.0, 0,
+                                      P(1), 4, P(1), P(1), P(1), P(0)) == 1
