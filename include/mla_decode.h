@@ -213,8 +213,9 @@ int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int h
  *                -inf is no sink.  Values must be finite or -inf.
  *   bmm1_scale : fp32 [1]; when set, replaces softmax_scale (same page: the
  *                fused bmm1/bmm2 scales may be device tensors, which then
- *                take precedence).  Read on the device, so it is not
- *                validated: a negative or NaN value acts as 0+.
+ *                take precedence).  Read on the device, so it cannot be
+ *                validated on the host: a NaN, negative or infinite value
+ *                makes every element of out and lse NaN.
  *   bmm2_scale : fp32 [1]; when set, replaces v_scale.
  *   kv_rope    : split cache (Ascend ATB MLA page, cacheMode KROPE_CTKV:
  *                ctKV [num_blocks, block_size, kv_heads, 512] and kRope

@@ -677,6 +677,14 @@ __device__ __forceinline__ int xcd_part(int w, int n) {
   return x * q + min(x, r) + i;
 }
 
+// True when a device-held bmm1 scale is NaN, negative or infinite (the host
+// rejects such values for the host-side scale).
+__device__ __forceinline__ bool bad_device_scale(const DecodeArgs &a) {
+  if (!a.bmm1_dev) return false;
+  const float v = *a.bmm1_dev;
+  return !(v >= 0.f && v < __builtin_inff());
+}
+
 // kAnyBlock: the cache's block size is a.page_size (a multiple of 16) rather
 // than the 64 tokens of a page, whose slice arithmetic is then shifts.
 template <bool kFp8, bool kSplit, bool kAnyBlock>
@@ -707,8 +715,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const bool active = wrow0 < a.rows;                 // wave-uniform
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   // A device-held bmm1 scale replaces the host value (FlashInfer MLA page:
-  // bmm1_scale / bmm2_scale may be device tensors); negative or NaN values
-  // act as 0+.
+  // bmm1_scale / bmm2_scale may be device tensors).  It cannot be validated
+  // on the host: a NaN, negative or infinite value makes every output NaN.
+  const bool bad_scale = bad_device_scale(a);
   const float scale_log2 = fmaxf(a.bmm1_dev ? *a.bmm1_dev * kLog2e : a.scale_log2, 1e-30f);
 
   const int elem = kFp8 ? 1 : 2;
@@ -930,7 +939,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         lt = l * am + __builtin_amdgcn_exp2f(zs - mm);
         inv = am / lt;
       }
-      const float lse_v = lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
+      if (bad_scale) inv = __builtin_nanf("");
+      const float lse_v = bad_scale ? __builtin_nanf("") : lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       const float v_scale = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
@@ -1106,7 +1116,8 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
     const float zero[kSlots][8] = {};
     fold_state(mu, Z, acc, a.sinks[h], 1.f, zero);
   }
-  const float inv = Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
+  const bool bad_scale = bad_device_scale(a);
+  const float inv = bad_scale ? __builtin_nanf("") : Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
   // Slot j of the unit is chunk slot 2t + pp = kSlots g + j: this lane
   // holds dims 32t + 16pp + 4hl + {0..3} (acc[j][0..3]) and + 8 (acc[j][4..7]).
   // v_permlane32_swap with lane ^ 32 forms whole 16-byte chunks: lanes < 32
@@ -1125,7 +1136,7 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
     if (row < a.rows) *(u32x4 *)(orow + 32 * t + 16 * pp) = u32x4{s0[0], s1[0], s0[1], s1[1]};
   }
   if (g == 0 && lane < 32 && row < a.rows)
-    a.lse[((long)b * a.hq + h) * a.s_q + qi] = Z > 0.f ? mu + __logf(Z) : kNegInf;
+    a.lse[((long)b * a.hq + h) * a.s_q + qi] = bad_scale ? __builtin_nanf("") : Z > 0.f ? mu + __logf(Z) : kNegInf;
 }
 
 }  // namespace

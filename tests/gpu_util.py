@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 import mla_paged_kv_metadata_amd as mla
+from oracle import fused_fp8_scales
 from oracle import mla_decode as oracle_decode
 
 DV = 512
@@ -25,9 +26,11 @@ def to_gpu(w, dev="cuda:0"):
 
 
 def scales(w):
+    """(bmm1, bmm2) for the workload: 1/sqrt(576) and 1 for a bf16 cache; the
+    oracle's fused fp8 scales (FlashInfer MLA page) for an e4m3fn cache."""
     if w.kv_dtype == "bf16":
         return w.head_dim ** -0.5, 1.0
-    return mla.fp8_fused_scales(k_scale=w.k_scale, v_scale=w.v_scale, head_dim_qk=w.head_dim)
+    return fused_fp8_scales(k_scale=w.k_scale, v_scale=w.v_scale, head_dim_qk=w.head_dim)
 
 
 def run_gpu(w, num_parts=None, fixed_cost=None, tensors=None):

@@ -386,3 +386,17 @@ def test_block_size_is_bitwise_invisible(kv_dtype, P):
     o1, l1 = mla_decode(w.q_bits, w.kv, kv_dtype, w.block_table, w.cache_seqlens, DV, s, True)
     o2, l2 = mla_decode(r.q_bits, r.kv, kv_dtype, r.block_table, r.cache_seqlens, DV, s, True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_product_fp8_scale_helper_equals_the_oracle():
+    """The package's fp8_fused_scales (argument marshalling for callers) and the
+    oracle's fused_fp8_scales follow the same note of the FlashInfer MLA page;
+    they must agree exactly for any inputs."""
+    import mla_paged_kv_metadata_amd as mla
+    rng = np.random.default_rng(17)
+    for _ in range(50):
+        qs, ks, vs, os_, sm = rng.uniform(0.01, 4.0, 5)
+        hd = int(rng.choice([64, 192, 576]))
+        a = mla.fp8_fused_scales(q_scale=qs, k_scale=ks, v_scale=vs, o_scale=os_, sm_scale=sm, head_dim_qk=hd)
+        b = fused_fp8_scales(q_scale=qs, k_scale=ks, v_scale=vs, o_scale=os_, sm_scale=sm, head_dim_qk=hd)
+        assert a == b
