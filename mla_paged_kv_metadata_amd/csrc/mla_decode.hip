@@ -55,6 +55,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -139,14 +141,13 @@ __device__ __forceinline__ void stage_q_rows(const uint8_t *qblock, LDS_AS uint8
     lds_dma16<0, false>(qblock + (8 * R + r) * 1152 + 16 * (8 * c + (j ^ qsw(r, R))), region + 1024 * i);
   }
 }
+__device__ __forceinline__ const LDS_AS bf16x8 *q_row_chunk(const LDS_AS uint8_t *region, int n, int C) {
+  return (const LDS_AS bf16x8 *)(region + 1024 * (9 * (n >> 3) + (C >> 3)) + 16 * (8 * (n & 7) + ((C & 7) ^ qsw(n & 7, n >> 3))));
+}
 __device__ __forceinline__ void read_q_rows(const LDS_AS uint8_t *region, int lane, bf16x8 (&qf)[36]) {
   const int n = lane & 31, hl = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < 36; ++ks) {
-    const int C = 2 * ks + hl;
-    qf[ks] = *(const LDS_AS bf16x8 *)(region + 1024 * (9 * (n >> 3) + (C >> 3)) +
-                                       16 * (8 * (n & 7) + ((C & 7) ^ qsw(n & 7, n >> 3))));
-  }
+  for (int ks = 0; ks < 36; ++ks) qf[ks] = *q_row_chunk(region, n, 2 * ks + hl);
 }
 
 // HBM -> LDS copy of one bf16 page (64 rows x 1152 B) into the layout above,
@@ -564,6 +565,262 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   return __ballot(need) != 0;
 }
 
+// ---------------------------------------------------------------------------
+// fp8 (e4m3fn) cache on the fp8 matrix core: v_mfma_scale_f32_32x32x64_f8f6f4.
+//
+// A 32x32x64 8-bit operand holds 32 bytes per lane: lane (row c, half h),
+// byte j is k = 16h + (j & 15) + 32 (j >> 4), and bytes 0..15 / 16..31 take
+// the E8M0 block scale of lane c / lane c + 32 (two 32-k scale blocks per
+// row; both checked on the device with integer test vectors).
+//
+//  * S^T = K Q^T per 64-dim k-block kb: k <-> dim 64 kb + k.  K (codes, scale
+//    1) is the A operand, straight from the LDS page.  q (bf16) enters as two
+//    e4m3 terms, q = 2^-e (hi + lo / 16), with one power-of-two e per head
+//    that puts the head's largest |q| in [128, 256): hi = e4m3(2^e q),
+//    lo = e4m3(16 (2^e q - hi)); the B scales 2^-e and 2^-(e+4) undo the
+//    factors, so S^T accumulates sum_d code_d q_d with about 8 significant
+//    bits of q (bf16 has 8).
+//  * O^T += V^T P^T over all 64 tokens in one k-step: k <-> token tau(h, j) =
+//    32 (j >> 4) + 8 ((j & 15) / 4) + 4h + (j & 3), which is where the S^T
+//    accumulator of lane (c, h) already holds its 32 scores (tile j >> 4,
+//    element j & 15), so P^T needs no lane exchange.  P enters as one e4m3
+//    term per 32-token tile with a power-of-two block scale 2^E (E = the
+//    tile's largest exponent), and the row sum l adds up the same rounded
+//    values, so the normalised weights stay consistent.
+// ---------------------------------------------------------------------------
+
+// bf16 chunk (8 dims) of q that lane half h places in slot i (0..3) of
+// k-block kb: slots 0-1 are bytes 0..15 (dims 64kb + 16h ..), slots 2-3
+// bytes 16..31 (dims 64kb + 32 + 16h ..).
+__device__ __forceinline__ int q_chunk_f8(int kb, int i, int h) { return 8 * kb + 2 * h + (i & 1) + 4 * (i >> 1); }
+
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }   // e in [-126, 127]
+
+// Packs four floats as e4m3 codes (round to nearest even; every input here
+// is within the format's range) into one dword, byte i = x[i].
+__device__ __forceinline__ unsigned pack_e4m3(float a, float b, float c, float d) {
+  v2i16 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 1.0f, true);
+  return __builtin_bit_cast(unsigned, w);
+}
+// The four e4m3 codes of a dword as floats.
+__device__ __forceinline__ f32x4 unpack_e4m3(unsigned v) {
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v, 1.0f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v, 1.0f, true);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// In place: q8[2kb] / q8[2kb+1] hold the bf16 q values of k-block kb's bytes
+// 0..15 / 16..31 (16 bf16 each, loaded by q_chunk_f8); they become the hi and
+// lo e4m3 terms (32 codes each).  s_hi / s_lo: the B-operand E8M0 scales.
+__device__ __forceinline__ void quantize_q_f8(i32x8 (&q8)[18], int &s_hi, int &s_lo) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 18; ++i)
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      mx = fmaxf(mx, fmaxf(fabsf(bf16_lo((unsigned)q8[i][w])), fabsf(bf16_hi((unsigned)q8[i][w]))));
+  mx = max_across_halves(mx);                     // the head's largest |q| (both lane halves)
+  // mx = f 2^x, f in [1, 2): e = 7 - x puts 2^e mx in [128, 256).
+  const int x = ((__float_as_int(mx) >> 23) & 255) - 127;
+  const int e = mx > 0.f ? max(-120, min(120, 7 - x)) : 0;
+  const float up = pow2f(e);
+  s_hi = 127 - e;
+  s_lo = 127 - e - 4;
+#pragma unroll
+  for (int kb = 0; kb < 9; ++kb) {
+    float v[32];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      v[2 * w] = bf16_lo((unsigned)q8[2 * kb][w]) * up;
+      v[2 * w + 1] = bf16_hi((unsigned)q8[2 * kb][w]) * up;
+      v[16 + 2 * w] = bf16_lo((unsigned)q8[2 * kb + 1][w]) * up;
+      v[16 + 2 * w + 1] = bf16_hi((unsigned)q8[2 * kb + 1][w]) * up;
+    }
+    i32x8 hi, lo;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const unsigned h = pack_e4m3(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3]);
+      const f32x4 hv = unpack_e4m3(h);
+      hi[d] = (int)h;
+      lo[d] = (int)pack_e4m3(16.f * (v[4 * d] - hv[0]), 16.f * (v[4 * d + 1] - hv[1]), 16.f * (v[4 * d + 2] - hv[2]),
+                             16.f * (v[4 * d + 3] - hv[3]));
+    }
+    q8[2 * kb] = hi;
+    q8[2 * kb + 1] = lo;
+  }
+}
+
+// Score steps on the fp8 matrix core with the accumulator in ordinary VGPRs
+// (see mfma_qk_first); sa / sb: the E8M0 scales of the A and B operands.
+__device__ __forceinline__ void mfma8_first(f32x16 &s, const i32x8 &a, const i32x8 &b, int sa, int sb) {
+  asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+      : "=&v"(s) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void mfma8(f32x16 &s, const i32x8 &a, const i32x8 &b, int sa, int sb) {
+  asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+      : "+v"(s) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// One 64-token fp8 page for this wave's 32 rows on the fp8 matrix core (the
+// fp8 counterpart of attend_page; same reference-max scheme and return).
+template <bool kSplit>
+__device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i32x8 (&q8)[18], int s_hi, int s_lo,
+                                               f32x16 (&o)[kOTiles], float &m, float &l, float &lq, float &m_restart,
+                                               int lane, int key0, int nvis, float scale_log2, bool mask,
+                                               const NextPage &nx) {
+  const int hl = lane >> 5;
+  const int r = lane & 31;
+  const int k127 = 127;                            // scale 1 for the cache codes
+
+  // K of token r (+32 for tile 1), k-block kb: bytes 0..15 are chunk hl and
+  // bytes 16..31 chunk 2 + hl of group kb, at 4096 kb + 64 t + 16 (chunk ^
+  // ((t >> 2) & 3)) in the fp8 page layout: two lane bases plus immediates.
+  const int f = (r >> 2) & 3;
+  const LDS_AS uint8_t *ka = pg + 64 * r + 16 * (hl ^ f);
+  const LDS_AS uint8_t *kc = pg + 64 * r + 16 * ((2 + hl) ^ f);
+  auto kload = [&](int kb, int tile) -> i32x8 {
+    const u32x4 x = *(const LDS_AS u32x4 *)(ka + 4096 * kb + 2048 * tile);
+    const u32x4 y = *(const LDS_AS u32x4 *)(kc + 4096 * kb + 2048 * tile);
+    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+  };
+  // V^T of dim tile mt by four 8-bit transposing reads (R = 0..3: bytes
+  // 8R .. 8R+7 = tokens 16R + 8 (e / 4) + 4h + (e % 4), e = 0..7).  In each
+  // 16-lane group G output lane i gets byte i % 8 of the rows loaded by lanes
+  // 2e + i / 8, so source lane (G, s) loads token 16R + 8 (s / 8) + 4 (G / 2)
+  // + (s / 2) % 4, dims 32 mt + 16 (G % 2) + 8 (s % 2): chunk 2 (mt % 2) +
+  // G % 2 of group mt / 2, swizzled by ((t >> 2) & 3) = (2 (s / 8) + G / 2) & 3.
+  const int G = lane >> 4, sl16 = lane & 15;
+  const int fv = (2 * (sl16 >> 3) + (G >> 1)) & 3;
+  const int vlane = 64 * (8 * (sl16 >> 3) + 4 * (G >> 1) + ((sl16 >> 1) & 3)) + 8 * (sl16 & 1);
+  const LDS_AS uint8_t *vb0 = pg + vlane + 16 * ((G & 1) ^ fv);
+  const LDS_AS uint8_t *vb1 = pg + vlane + 16 * ((2 + (G & 1)) ^ fv);
+  auto vload = [&](int mt) -> i32x8 {
+    const LDS_AS uint8_t *p = ((mt & 1) ? vb1 : vb0) + 4096 * (mt >> 1);
+    const v2i32 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)p);
+    const v2i32 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 1024));
+    const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 2048));
+    const v2i32 d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 3072));
+    return i32x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  };
+
+  // Online softmax of one 32-token tile in 17 pieces (as in attend_page): in
+  // S^T a lane holds head r and tokens (i/4)*8 + 4*hl + i%4 of the tile.
+  // Piece 6 also fixes the tile's block exponent E = floor(t - mu), t the
+  // tile's largest scaled score, so that P' = 2^(s - mu - E) lies in (0, 2);
+  // pieces 7-14 also sum P' exactly; piece 15 rounds P' to e4m3 (4 dwords)
+  // and sums the rounded values; piece 16 adds 2^E times both sums (over
+  // both lane halves) to l (exact, for lse) and lq (rounded, the normaliser
+  // of the output, so that the weights it divides sum to one).
+  float mx = kNegInf, ps = 0.f, psq = 0.f, mu = 0.f;
+  int et[2] = {0, 0};
+  bool need = false;
+  u32x4 p8[2];
+  auto soft = [&](f32x16 &sc, int tile, int tok0, int piece) {
+    if (piece < 2) {
+      if (mask) {
+#pragma unroll
+        for (int i = 8 * piece; i < 8 * piece + 8; ++i) {
+          const int tok = tok0 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          if (tok >= nvis) sc[i] = kNegInf;
+        }
+      }
+    } else if (piece < 6) {
+      const int i0 = 4 * (piece - 2);
+      const float t = fmaxf(fmaxf(sc[i0], sc[i0 + 1]), fmaxf(sc[i0 + 2], sc[i0 + 3]));
+      mx = piece == 2 ? t : fmaxf(mx, t);
+    } else if (piece == 6) {
+      float t = max_across_halves(mx);
+      t = (t == kNegInf) ? kNegInf : t * scale_log2;
+      if (m == kNegInf) m = t;                          // first visible keys fix the reference
+      const bool nd = t > m + kRefSlackLog2;
+      if (nd) m_restart = fmaxf(m_restart, t);
+      need |= nd;
+      mu = (m == kNegInf) ? 0.f : m;
+      const int e = t == kNegInf ? 0 : (int)floorf(t - mu);
+      et[tile] = max(-100, min(100, e));
+      mu += (float)et[tile];
+    } else if (piece < 15) {
+      const int i0 = 2 * (piece - 7);
+      sc[i0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0], scale_log2, -mu));
+      sc[i0 + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0 + 1], scale_log2, -mu));
+      ps = (piece == 7 ? 0.f : ps) + (sc[i0] + sc[i0 + 1]);
+    } else if (piece == 15) {
+      psq = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const unsigned c = pack_e4m3(sc[4 * d], sc[4 * d + 1], sc[4 * d + 2], sc[4 * d + 3]);
+        p8[tile][d] = c;
+        const f32x4 back = unpack_e4m3(c);
+        psq += (back[0] + back[1]) + (back[2] + back[3]);
+      }
+    } else {
+      const float w = pow2f(et[tile]);
+      l += sum_across_halves(ps) * w;
+      lq += sum_across_halves(psq) * w;
+    }
+  };
+  constexpr int kSoftPieces = 17;
+
+  // S^T = K Q^T: step g = 9 tile + kb runs the hi and lo MFMAs of k-block kb
+  // (one accumulation chain per tile); K fragments two steps ahead; one copy
+  // instruction of the next page every second step (9 per fp8 page).
+  constexpr int kPre = 2;
+  i32x8 kf[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) kf[i] = kload(i, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s0, s1;
+  auto qk_step = [&](f32x16 &sc, int tile, int kb) {
+    const int g = tile * 9 + kb, sl = g % kPre;
+    if (kb == 0) mfma8_first(sc, kf[sl], q8[0], k127, s_hi);
+    else mfma8(sc, kf[sl], q8[2 * kb], k127, s_hi);
+    mfma8(sc, kf[sl], q8[2 * kb + 1], k127, s_lo);
+    if (g + kPre < 18) kf[sl] = kload((g + kPre) % 9, (g + kPre) / 9);
+    if (nx.valid && g < 9) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g);
+  };
+#pragma unroll
+  for (int kb = 0; kb < 9; ++kb) {
+    qk_step(s0, 0, kb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Tile 1, with tile 0's softmax: two pieces after each of its steps.
+#pragma unroll
+  for (int kb = 0; kb < 9; ++kb) {
+    qk_step(s1, 1, kb);
+    if (kb == 0) mfma_qk_drain(s0);
+#pragma unroll
+    for (int pc = 2 * kb; pc < 2 * kb + 2; ++pc)
+      if (pc < kSoftPieces) soft(s0, 0, key0, pc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // First V^T operands, then tile 1's softmax.
+  constexpr int kVPre = 2;
+  i32x8 vf[kVPre];
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) vf[i] = vload(i);
+  mfma_qk_drain(s1);
+#pragma unroll
+  for (int pc = 0; pc < kSoftPieces; ++pc) soft(s1, 1, key0 + 32, pc);
+  // P^T: bytes 0..15 tile 0, bytes 16..31 tile 1; lane half h supplies the
+  // block scale of tile h.
+  const i32x8 pt = {(int)p8[0][0], (int)p8[0][1], (int)p8[0][2], (int)p8[0][3],
+                    (int)p8[1][0], (int)p8[1][1], (int)p8[1][2], (int)p8[1][3]};
+  const int ps_scale = 127 + (hl ? et[1] : et[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mt = 0; mt < kOTiles; ++mt) {
+    const int sl = mt % kVPre;
+    o[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[sl], pt, o[mt], 0, 0, 0, k127, 0, ps_scale);
+    if (mt + kVPre < kOTiles) vf[sl] = vload(mt + kVPre);
+    __builtin_amdgcn_sched_barrier(0);               // keep the V^T loads kVPre steps ahead
+  }
+  return __ballot(need) != 0;
+}
+
 // Number of passes a segment may take when a score overshoots the reference
 // max by more than kRefSlackLog2 (see attend_page).  Bounded so that a
 // workgroup always terminates; a further overshoot in the last pass is
@@ -746,19 +1003,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   auto seq_len = [&](int b) { return (int)max(0L, min((long)a.seqlens[b], (long)a.max_blocks * bs)); };
   auto seq_end = [&](int b, int nblk) { return b == b1 ? max(0, min(md[3], nblk)) : nblk; };
 
-  bf16x8 qf[kKSteps];
-  // This lane's q fragments: row (qi, h) of sequence b, dims 16 ks + 8 hl .. +7.
-  // The rope columns (k-steps 32..35) come from q_rope when q is split
-  // (Ascend ATB MLA page: qNope [.., 512] and qRope [.., 64]).
+  // q of this lane's row for the bf16 matrix core (qf: dims 16 ks + 8 hl ..
+  // +7) or, with an fp8 cache, for the fp8 matrix core (q8: bf16 chunks
+  // q_chunk_f8 until quantize_q_f8 turns them into the hi / lo e4m3 terms at
+  // the start of the split).
+  bf16x8 qf[kFp8 ? 1 : kKSteps];
+  i32x8 q8[kFp8 ? 18 : 1];
+  int s_hi = 127, s_lo = 127;
+  auto set_q8_chunk = [&](int kb, int i, const bf16x8 &v) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) q8[2 * kb + (i >> 1)][4 * (i & 1) + d] = (int)w[d];
+  };
+  // Row (qi, h) of sequence b.  The rope columns (chunks 64..71) come from
+  // q_rope when q is split (Ascend ATB MLA page: qNope [.., 512] and qRope
+  // [.., 64]).
   auto load_q = [&](int b) {
     const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
     const long r = ((long)min(b, a.batch - 1) * a.s_q + c.qi) * a.hq + c.h;
-    const int hl8 = 8 * (lane_id_here() >> 5);
-    const uint16_t *qn = a.q + r * a.q_stride + hl8;
-    const uint16_t *qr = a.q_rope ? a.q_rope + r * (kHeadDim - kHeadDimV) + hl8 : qn + kHeadDimV;
+    if constexpr (kFp8) {
+      const int hl = lane_id_here() >> 5;
+      const uint16_t *qn = a.q + r * a.q_stride;
+      const uint16_t *qr = a.q_rope ? a.q_rope + r * (kHeadDim - kHeadDimV) : qn + kHeadDimV;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = *(const bf16x8 *)(ks < kHeadDimV / 16 ? qn + 16 * ks : qr + 16 * (ks - kHeadDimV / 16));
+      for (int kb = 0; kb < 9; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int C = q_chunk_f8(kb, i, hl);        // 8 dims, C in 0..71
+          set_q8_chunk(kb, i, *(const bf16x8 *)(C < kHeadDimV / 8 ? qn + 8 * C : qr + 8 * (C - kHeadDimV / 8)));
+        }
+    } else {
+      // dims 16 ks + 8 hl .. +7
+      const int hl8 = 8 * (lane_id_here() >> 5);
+      const uint16_t *qn = a.q + r * a.q_stride + hl8;
+      const uint16_t *qr = a.q_rope ? a.q_rope + r * (kHeadDim - kHeadDimV) + hl8 : qn + kHeadDimV;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        qf[ks] = *(const bf16x8 *)(ks < kHeadDimV / 16 ? qn + 16 * ks : qr + 16 * (ks - kHeadDimV / 16));
+    }
   };
 
   int cur = 0;              // buffer that receives / holds the next page to process
@@ -796,7 +1078,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       LDS_AS uint8_t *region = smem + wave * 32 * kHeadDim * 2;
       stage_q_rows(qblock, region, lane);
       wait_vmcnt<0>();
-      read_q_rows(region, lane, qf);
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int kb = 0; kb < 9; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x8 v = *q_row_chunk(region, lane & 31, q_chunk_f8(kb, i, lane >> 5));
+            set_q8_chunk(kb, i, v);
+          }
+      } else {
+        read_q_rows(region, lane, qf);
+      }
       __syncthreads();                                // q read back before the page lands on it
     }
     if (hi0 > first0) {                               // then the split's first page is first0
@@ -841,7 +1133,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     }
     if (tid == 0) *rerun_flag = 0;
 
-    float m = kNegInf, l = 0.f, m_restart = kNegInf;
+    // l: the row sum of the probabilities; lq: with an fp8 cache, the sum of
+    // the same probabilities as rounded for the matrix core (the output's
+    // normaliser); equal to l otherwise.
+    float m = kNegInf, l = 0.f, lq = 0.f, m_restart = kNegInf;
     // O^T accumulators start as the result of an all-zero MFMA so that they
     // live in accumulation registers from the first page on.
     f32x16 o[kOTiles];
@@ -866,6 +1161,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         const int t = slice_tok(j);
         return src_of(block_of(min(t / bs, nent - 1)), t % bs);
       };
+      if constexpr (kFp8) quantize_q_f8(q8, s_hi, s_lo);
       for (int pass = 0;; ++pass) {
         bool need = false;
         if (!have_first) {
@@ -891,8 +1187,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           nx.wave = wave;
           const LDS_AS uint8_t *pg = bufs[cur];
           if (active) {
-            need |= attend_page<kFp8, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
-                                      (j + 1) * kPage > nvis_min, nx);
+            if constexpr (kFp8)
+              need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
+                                             scale_log2, (j + 1) * kPage > nvis_min, nx);
+            else
+              need |= attend_page<false, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
+                                                 (j + 1) * kPage > nvis_min, nx);
           } else if (nx.valid) {                    // a wave without rows still copies its share
             if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
             else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
@@ -912,6 +1212,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         if (m_restart != kNegInf) m = m_restart;
         m_restart = kNegInf;
         l = 0.f;
+        lq = 0.f;
         mfma_zero_all(o);
       }
     }
@@ -936,8 +1237,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       float lt = 0.f, inv = 0.f;
       if (mm != kNegInf) {
         const float am = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mm);
-        lt = l * am + __builtin_amdgcn_exp2f(zs - mm);
-        inv = am / lt;
+        const float zt = __builtin_amdgcn_exp2f(zs - mm);
+        lt = l * am + zt;
+        // O holds sum_t p~_t v_t with the rounded weights p~ of an fp8 cache:
+        // normalise by their sum (scaled to lt) so that they add up to one.
+        inv = kFp8 ? (lq > 0.f ? l * am / (lt * lq) : 0.f) : am / lt;
       }
       if (bad_scale) inv = __builtin_nanf("");
       const float lse_v = bad_scale ? __builtin_nanf("") : lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
