@@ -101,10 +101,12 @@ def gather_rows(kv: np.ndarray, block_table_row: np.ndarray, L: int, page_block_
     return np.concatenate(pages, axis=0)[:L]
 
 
-def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, v_scale: float = 1.0, sink=None):
+def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale, v_scale=1.0, sink=None):
     """Softmax attention of query rows qh (G, D) over keys K (n, D), values V (n, Dv).
 
     Returns (out (G, Dv), lse (G,)) with lse = ln sum_j exp(scale * q.k_j).
+    ``scale`` and ``v_scale`` are scalars or per-row (G,) factors (the per-head
+    qkDescale / pvDescale of the Ascend ATB MLA page fold into them).
     n == 0 gives out = 0, lse = -inf.  With ``sink`` (G,) (FlashInfer MLA
     page, ``sinks``: a per-head extra term of the softmax denominator, read as
     a logit): the denominator is sum_j exp(s_j) + exp(sink), lse includes the
@@ -112,6 +114,8 @@ def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, v_scale: 
     """
     G = qh.shape[0]
     n = K.shape[0]
+    scale = np.broadcast_to(np.asarray(scale, dtype=np.float64), (G,))[:, None]
+    v_scale = np.broadcast_to(np.asarray(v_scale, dtype=np.float64), (G,))[:, None]
     if sink is None:
         if n == 0:
             return np.zeros((G, V.shape[1])), np.full(G, -np.inf)
@@ -156,19 +160,26 @@ def lse_merge(outs, lses):
 
 
 def mla_decode_f64(q: np.ndarray, rows_of, cache_seqlens, num_heads_k: int, head_dim_v: int,
-                   softmax_scale: float, causal: bool, v_scale: float = 1.0, batches=None, sinks=None):
+                   softmax_scale: float, causal: bool, v_scale: float = 1.0, batches=None, sinks=None,
+                   qk_descale=None, pv_descale=None):
     """Core oracle on float64 operands.
 
     q: (B, s_q, H_q, D) float64.  rows_of(b) -> (L_b, H_k, D) float64, the
     sequence's cached rows in logical order.  Returns out (B, s_q, H_q, Dv) and
     lse (B, H_q, s_q) float64.  ``batches`` restricts the work to some b (the
     other entries stay 0 / -inf).  ``sinks``: None or (H_q,) per-head sink
-    logits (see attend).
+    logits (see attend).  ``qk_descale`` / ``pv_descale``: None or (H_q,)
+    per-head factors (Ascend ATB MLA page, qkDescale / pvDescale [num_heads]):
+    head h's scores are softmax_scale * qk_descale[h] * q.k and its output is
+    multiplied by v_scale * pv_descale[h]; lse follows the scores, the sink
+    logits are not rescaled.
     """
     B, s_q, H, D = q.shape
     if H % num_heads_k:
         raise ValueError("num_heads_q must be a multiple of num_heads_k")
     G = H // num_heads_k
+    qk = np.ones(H) if qk_descale is None else np.asarray(qk_descale, dtype=np.float64)
+    pv = np.ones(H) if pv_descale is None else np.asarray(pv_descale, dtype=np.float64)
     out = np.zeros((B, s_q, H, head_dim_v))
     lse = np.full((B, H, s_q), -np.inf)
     for b in (range(B) if batches is None else batches):
@@ -181,7 +192,7 @@ def mla_decode_f64(q: np.ndarray, rows_of, cache_seqlens, num_heads_k: int, head
                 K = rows[:n, hk, :]
                 V = K[:, :head_dim_v]
                 hs = slice(hk * G, (hk + 1) * G)
-                o, l = attend(q[b, i, hs, :], K, V, softmax_scale, v_scale,
+                o, l = attend(q[b, i, hs, :], K, V, softmax_scale * qk[hs], v_scale * pv[hs],
                               None if sinks is None else np.asarray(sinks, dtype=np.float64)[hs])
                 out[b, i, hs, :] = o
                 lse[b, hs, i] = l
@@ -189,15 +200,20 @@ def mla_decode_f64(q: np.ndarray, rows_of, cache_seqlens, num_heads_k: int, head
 
 
 def mla_decode(q_bits, kv_raw, kv_format, block_table, cache_seqlens, head_dim_v, softmax_scale,
-               causal=False, v_scale=1.0, batches=None, sinks=None):
+               causal=False, v_scale=1.0, batches=None, sinks=None, q_format="bf16", qk_descale=None,
+               pv_descale=None):
     """Oracle on the raw input bytes the GPU also receives.
 
-    q_bits: (B, s_q, H_q, D) uint16 bf16 bits.  kv_raw: (num_blocks, P, H_k, D)
-    uint16 bf16 bits or uint8 e4m3fn codes.  softmax_scale is the full factor on
-    q.k (bmm1 for an fp8 cache); v_scale multiplies the weighted sum (bmm2).
-    Only the pages a sequence uses are decoded.
+    q_bits: (B, s_q, H_q, D) uint16 bf16 bits, or uint8 e4m3fn codes when
+    q_format is "fp8_e4m3fn" (FlashInfer MLA page, note on fused scales: an
+    fp8 query's q_scale is folded into bmm1_scale, so the codes enter the
+    product unscaled).  kv_raw: (num_blocks, P, H_k, D) uint16 bf16 bits or
+    uint8 e4m3fn codes.  softmax_scale is the full factor on q.k (bmm1 for an
+    fp8 cache); v_scale multiplies the weighted sum (bmm2).  qk_descale /
+    pv_descale: see mla_decode_f64.  Only the pages a sequence uses are
+    decoded.
     """
-    q = bf16_bits_to_f64(q_bits)
+    q = decode_kv(q_bits, q_format)
     P = kv_raw.shape[1]
     Hk = kv_raw.shape[2]
 
@@ -206,4 +222,4 @@ def mla_decode(q_bits, kv_raw, kv_format, block_table, cache_seqlens, head_dim_v
         return decode_kv(gather_rows(kv_raw, block_table[b], L, P), kv_format)
 
     return mla_decode_f64(q, rows_of, cache_seqlens, Hk, head_dim_v, softmax_scale, causal, v_scale, batches,
-                          sinks)
+                          sinks, qk_descale, pv_descale)

@@ -400,3 +400,100 @@ def test_product_fp8_scale_helper_equals_the_oracle():
         a = mla.fp8_fused_scales(q_scale=qs, k_scale=ks, v_scale=vs, o_scale=os_, sm_scale=sm, head_dim_qk=hd)
         b = fused_fp8_scales(q_scale=qs, k_scale=ks, v_scale=vs, o_scale=os_, sm_scale=sm, head_dim_qk=hd)
         assert a == b
+
+
+# ------------------------------------------------------------------ fp8 query, per-head descales
+
+def _e4m3_codes(rng, shape):
+    """Random finite e4m3fn codes of moderate magnitude (exponent field 3..10,
+    so |value| lies in [2^-4, 2^4)), both signs."""
+    e = rng.integers(3, 11, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    sgn = rng.integers(0, 2, size=shape)
+    return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_fp8_query_dequantise_then_attend(kv_dtype):
+    """An e4m3 query with q_scale folded into bmm1 (FlashInfer MLA page, note on
+    fused scales) equals the bf16 query q_scale * code with the plain scale: a
+    power-of-two q_scale keeps every q_scale * code exact in bf16."""
+    w = make_workload(seqlens=[70, 3, 130], num_heads_q=8, kv_dtype=kv_dtype, seed=23)
+    rng = np.random.default_rng(24)
+    codes = _e4m3_codes(rng, w.q_bits.shape)
+    q_scale = 2.0 ** -3
+    base = 1 / 24 if kv_dtype == "bf16" else w.k_scale / 24
+    vs = 1.0 if kv_dtype == "bf16" else w.v_scale
+    o1, l1 = mla_decode(codes, w.kv, kv_dtype, w.block_table, w.cache_seqlens, DV, q_scale * base, False, vs,
+                        q_format="fp8_e4m3fn")
+    qv = (q_scale * E4M3FN_TABLE[codes]).astype(np.float32)
+    qb = bf16_bits_from_f32(qv)
+    assert np.array_equal(bf16_bits_to_f64(qb), q_scale * E4M3FN_TABLE[codes])     # exact in bf16
+    o2, l2 = mla_decode(qb, w.kv, kv_dtype, w.block_table, w.cache_seqlens, DV, base, False, vs)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(l1, l2, rtol=1e-12, atol=1e-14)
+    # and the codes really matter: a wrong decode of the query changes the result
+    o3, _ = mla_decode(codes.astype(np.uint16), w.kv, kv_dtype, w.block_table, w.cache_seqlens, DV, base, False,
+                       vs)
+    assert not np.allclose(o1, o3)
+
+
+def test_fp8_query_and_cache_equal_dequantised_operands():
+    """Both operands as codes with the fused scales equal dequantise-then-attend
+    with scale 1/sqrt(576) and unit v_scale (P13 with a quantised query)."""
+    w = make_workload(seqlens=[40, 90], num_heads_q=4, kv_dtype="fp8_e4m3fn", seed=25)
+    codes = _e4m3_codes(np.random.default_rng(26), w.q_bits.shape)
+    q_s = 0.37
+    b1, b2 = fused_fp8_scales(q_scale=q_s, k_scale=w.k_scale, v_scale=w.v_scale)
+    o1, l1 = mla_decode(codes, w.kv, "fp8_e4m3fn", w.block_table, w.cache_seqlens, DV, b1, False, b2,
+                        q_format="fp8_e4m3fn")
+    q = q_s * E4M3FN_TABLE[codes]
+    deq = w.k_scale * E4M3FN_TABLE[w.kv]
+    o2, l2 = mla_decode_f64(q, lambda b: gather_rows(deq, w.block_table[b], int(w.cache_seqlens[b]), 64),
+                            w.cache_seqlens, 1, DV, 1 / 24, False, 1.0)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(l1, l2, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_qk_descale_equals_a_per_head_scaled_query(causal):
+    """qkDescale[h] (Ascend ATB MLA page) multiplies head h's scores: with
+    power-of-two factors this equals scaling head h's query rows exactly.
+    Distinct factors per head and two KV heads catch a wrong head mapping."""
+    w = make_workload(seqlens=[50, 1, 129], s_q=2, num_heads_q=8, num_heads_k=2, causal=causal, seed=27)
+    d = 2.0 ** np.array([-2, -1, 0, 1, 2, 0, -1, 1], dtype=np.float64)
+    o1, l1 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal,
+                        qk_descale=d)
+    qd = bf16_bits_to_f64(w.q_bits) * d[None, None, :, None]
+    qb = bf16_bits_from_f32(qd.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(qb), qd)
+    o2, l2 = mla_decode(qb, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    fin = np.isfinite(l2)
+    assert np.array_equal(fin, np.isfinite(l1)) and np.allclose(l1[fin], l2[fin], rtol=1e-12)
+    o0, _ = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, causal)
+    assert not np.allclose(o0, o1)
+
+
+def test_pv_descale_scales_the_output_only():
+    """pvDescale[h] multiplies head h's output; lse does not depend on it."""
+    w = make_workload(seqlens=[33, 200], num_heads_q=6, num_heads_k=2, seed=28)
+    p = np.array([0.5, 2.0, 1.0, 3.0, -1.0, 0.25])
+    o0, l0 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24)
+    o1, l1 = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, pv_descale=p)
+    assert np.allclose(o1, o0 * p[None, None, :, None], rtol=1e-14, atol=0)
+    assert np.array_equal(l1, l0)
+
+
+def test_descales_leave_sinks_unscaled():
+    """A sink is a logit on the softmax's own scale: qkDescale scales the scores
+    and not the sink, so with one key the weight of the key is
+    e^(d s) / (e^(d s) + e^z)."""
+    w = make_workload(seqlens=[1], num_heads_q=2, seed=29)
+    d = np.array([2.0, 0.5])
+    z = np.array([0.3, -1.0])
+    o, l = mla_decode(w.q_bits, w.kv, "bf16", w.block_table, w.cache_seqlens, DV, 1 / 24, sinks=z, qk_descale=d)
+    k = bf16_bits_to_f64(w.kv[w.block_table[0, 0], 0, 0])
+    q = bf16_bits_to_f64(w.q_bits[0, 0])
+    s = d * (q @ k) / 24
+    wk = np.exp(s) / (np.exp(s) + np.exp(z))
+    assert np.allclose(o[0, 0], wk[:, None] * k[None, :DV], rtol=1e-12)
+    assert np.allclose(l[0, :, 0], np.logaddexp(s, z), rtol=1e-12)
