@@ -77,6 +77,11 @@ enum mla_kv_dtype {
   MLA_KV_FP8_E4M3FN = 1   /* cache rows are OCP FP8 E4M3 codes (finite max 448) */
 };
 
+enum mla_q_dtype {
+  MLA_Q_BF16 = 0,         /* q is bf16 */
+  MLA_Q_FP8_E4M3FN = 1    /* q is OCP FP8 E4M3 codes (mla_decode_fwd_ext only) */
+};
+
 /* Human-readable text for a status code (static storage; never NULL).  The
  * UNSUPPORTED text of the last failing call on this thread names the reason,
  * as the vLLM platform gate returns (supported, reason). */
@@ -231,6 +236,24 @@ int mla_combine_splits(const void *q, int batch, int s_q, int num_heads_q, int h
  *                mla_combine_splits only (the combine applies the sinks of
  *                split sequences and the device bmm2_scale, so it must get the
  *                same ext).  Other values are INVALID_ARG.
+ *   bmm1_scale_log2: fp32 [1]; when set, the factor on q.k in base 2, i.e.
+ *                bmm1_scale * log2(e) (FlashInfer MLA page: the device-scale
+ *                pair (bmm1_scale_log2_tensor, bmm2_scale_tensor)); it
+ *                replaces softmax_scale and bmm1_scale.  Not validated on the
+ *                host: a NaN, negative or infinite value makes out and lse NaN.
+ *   qk_descale : fp32 [num_heads_q]; head h's scores are multiplied by
+ *                qk_descale[h] on top of the scale (Ascend ATB MLA page,
+ *                qkDescale [num_heads]).  Sink logits are not rescaled.  A
+ *                NaN, negative or infinite entry makes head h's out and lse NaN.
+ *   pv_descale : fp32 [num_heads_q]; head h's output is multiplied by
+ *                pv_descale[h] on top of v_scale (Ascend ATB MLA page,
+ *                pvDescale [num_heads]); lse does not depend on it.
+ *   q_dtype    : MLA_Q_BF16 (0, default) or MLA_Q_FP8_E4M3FN (1): q holds
+ *                e4m3fn codes [batch][s_q][num_heads_q][576], whose q_scale
+ *                the caller folds into the scale (FlashInfer MLA page, note on
+ *                fused scales: bmm1 = q_scale * k_scale * sm_scale /
+ *                sqrt(576)).  An fp8 q must be joined (q_rope NULL) and
+ *                needs an fp8 cache; other pairings are UNSUPPORTED.
  * head_dim stays 576 (the total width) in every layout. */
 typedef struct mla_decode_ext {
   const float *sinks;
@@ -239,6 +262,10 @@ typedef struct mla_decode_ext {
   const void *kv_rope;
   const void *q_rope;
   int stages;
+  const float *bmm1_scale_log2;
+  const float *qk_descale;
+  const float *pv_descale;
+  int q_dtype;
 } mla_decode_ext;
 
 /* mla_decode_fwd with the optional inputs above (NULL ext = mla_decode_fwd). */

@@ -79,7 +79,21 @@ _DECODE_ARGTYPES = [
 class DecodeExt(ctypes.Structure):
     """mla_decode_ext of include/mla_decode.h."""
     _fields_ = [("sinks", _vp), ("bmm1_scale", _vp), ("bmm2_scale", _vp), ("kv_rope", _vp), ("q_rope", _vp),
-                ("stages", _c_int)]
+                ("stages", _c_int), ("bmm1_scale_log2", _vp), ("qk_descale", _vp), ("pv_descale", _vp),
+                ("q_dtype", _c_int)]
+
+
+Q_BF16 = 0
+Q_FP8_E4M3FN = 1
+
+
+# Status codes of include/mla_decode.h.
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_NO_DEVICE = 4
+MLA_ERR_HIP = 5
 
 
 class MlaError(RuntimeError):
@@ -193,7 +207,9 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
                    workspace: Optional[torch.Tensor] = None, stage: str = "all",
                    sinks: Optional[torch.Tensor] = None, bmm1_scale_tensor: Optional[torch.Tensor] = None,
                    bmm2_scale_tensor: Optional[torch.Tensor] = None, kv_rope: Optional[torch.Tensor] = None,
-                   q_rope: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   q_rope: Optional[torch.Tensor] = None, bmm1_scale_log2_tensor: Optional[torch.Tensor] = None,
+                   qk_descale: Optional[torch.Tensor] = None,
+                   pv_descale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode attention (FlashMLA interface page, flash_mla_with_kvcache).
 
     q (B, s_q, H_q, 576) bf16; kv_cache (num_blocks, page_block_size, H_k, 576)
@@ -212,13 +228,20 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
     v_scale; kv_rope (num_blocks, page_block_size, H_k, 64) with kv_cache
     then (num_blocks, page_block_size, H_k, 512) (split cache); q_rope
     (B, s_q, H_q, 64) bf16
-    with q then (B, s_q, H_q, 512) (split query).
+    with q then (B, s_q, H_q, 512) (split query); bmm1_scale_log2_tensor (1,)
+    fp32, bmm1 * log2(e), replacing softmax_scale and bmm1_scale_tensor;
+    qk_descale / pv_descale (H_q,) fp32 per-head factors on the scores / the
+    output.  q may be torch.float8_e4m3fn (joined layout only) with its
+    q_scale folded into the bmm1 scale.
     """
     lib = load_library()
     if softmax_scale is None:
         softmax_scale = HEAD_DIM ** (-0.5)
     dev = q.device
-    _need(q, "q", torch.bfloat16, dev)
+    q_fp8 = q.dtype == torch.float8_e4m3fn
+    _need(q, "q", torch.float8_e4m3fn if q_fp8 else torch.bfloat16, dev)
+    if q_fp8 and q_rope is not None:
+        raise ValueError("an fp8 q must be joined (no q_rope)")
     _need(kv_cache, "kv_cache", None, dev)
     _need(block_table, "block_table", torch.int32, dev)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev)
@@ -275,11 +298,17 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
         _need(sinks, "sinks", torch.float32, dev)
         if tuple(sinks.shape) != (Hq,):
             raise ValueError("sinks must be (num_heads_q,)")
-    for t, name in ((bmm1_scale_tensor, "bmm1_scale_tensor"), (bmm2_scale_tensor, "bmm2_scale_tensor")):
+    for t, name in ((bmm1_scale_tensor, "bmm1_scale_tensor"), (bmm2_scale_tensor, "bmm2_scale_tensor"),
+                    (bmm1_scale_log2_tensor, "bmm1_scale_log2_tensor")):
         if t is not None:
             _need(t, name, torch.float32, dev)
             if t.numel() != 1:
                 raise ValueError(f"{name} must hold one value")
+    for t, name in ((qk_descale, "qk_descale"), (pv_descale, "pv_descale")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != (Hq,):
+                raise ValueError(f"{name} must be (num_heads_q,)")
     stages = {"all": 3, "splits": 1, "combine": 2}[stage]
     args = (_ptr(q), B, s_q, Hq, D, _ptr(kv_cache), code, nb, page, hk,
             _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
@@ -287,9 +316,11 @@ def mla_decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.T
             _ptr(tile_scheduler_metadata), num_parts, _ptr(num_splits),
             _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev))
     with torch.cuda.device(dev):
-        if any(t is not None for t in (sinks, bmm1_scale_tensor, bmm2_scale_tensor, kv_rope, q_rope)):
+        if q_fp8 or any(t is not None for t in (sinks, bmm1_scale_tensor, bmm2_scale_tensor, kv_rope, q_rope,
+                                                 bmm1_scale_log2_tensor, qk_descale, pv_descale)):
             ext = DecodeExt(_ptr(sinks), _ptr(bmm1_scale_tensor), _ptr(bmm2_scale_tensor), _ptr(kv_rope),
-                            _ptr(q_rope), stages)
+                            _ptr(q_rope), stages, _ptr(bmm1_scale_log2_tensor), _ptr(qk_descale),
+                            _ptr(pv_descale), Q_FP8_E4M3FN if q_fp8 else Q_BF16)
             rc = lib.mla_decode_fwd_ext(*args, ctypes.byref(ext))
         else:
             fn = {3: lib.mla_decode_fwd, 1: lib.mla_decode_splits, 2: lib.mla_combine_splits}[stages]

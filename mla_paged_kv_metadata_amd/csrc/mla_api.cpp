@@ -218,6 +218,10 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
   a.sinks = nullptr;
   a.bmm1_dev = nullptr;
   a.bmm2_dev = nullptr;
+  a.bmm1_log2_dev = nullptr;
+  a.qk_descale = nullptr;
+  a.pv_descale = nullptr;
+  a.q_fp8 = 0;
   if (ext) {
     a.q_rope = (const uint16_t *)ext->q_rope;
     a.q_stride = ext->q_rope ? MLA_HEAD_DIM_V : MLA_HEAD_DIM;
@@ -225,6 +229,10 @@ static int decode_call(int stage, const void *q, int batch, int s_q, int num_hea
     a.sinks = ext->sinks;
     a.bmm1_dev = ext->bmm1_scale;
     a.bmm2_dev = ext->bmm2_scale;
+    a.bmm1_log2_dev = ext->bmm1_scale_log2;
+    a.qk_descale = ext->qk_descale;
+    a.pv_descale = ext->pv_descale;
+    a.q_fp8 = ext->q_dtype == MLA_Q_FP8_E4M3FN;
   }
   if (stage & 1) {
     hipError_t e = mla::launch_decode(a, (hipStream_t)stream);
@@ -288,6 +296,12 @@ int mla_decode_fwd_ext(const void *q, int batch, int s_q, int num_heads_q, int h
   if (ext) {
     if (ext->stages < 0 || ext->stages > 3) return fail(MLA_ERR_INVALID_ARG, "ext->stages must be 0, 1, 2 or 3");
     if (ext->stages) stage = ext->stages;
+    if (ext->q_dtype != MLA_Q_BF16 && ext->q_dtype != MLA_Q_FP8_E4M3FN)
+      return fail(MLA_ERR_UNSUPPORTED, "ext->q_dtype must be MLA_Q_BF16 or MLA_Q_FP8_E4M3FN");
+    if (ext->q_dtype == MLA_Q_FP8_E4M3FN && ext->q_rope)
+      return fail(MLA_ERR_UNSUPPORTED, "an fp8 q must be joined (q_rope NULL)");
+    if (ext->q_dtype == MLA_Q_FP8_E4M3FN && kv_dtype != MLA_KV_FP8_E4M3FN)
+      return fail(MLA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 cache (kv_dtype MLA_KV_FP8_E4M3FN)");
   }
   return decode_call(stage, q, batch, s_q, num_heads_q, head_dim, kv_cache, kv_dtype, num_blocks, page_block_size,
                      num_heads_k, block_table, max_blocks_per_seq, cache_seqlens, head_dim_v, softmax_scale, v_scale,

@@ -361,6 +361,12 @@ struct NextPage {
   bool valid;                 // workgroup-uniform
 };
 
+// A row's raw scores times its per-head qkDescale.
+__device__ __forceinline__ void scale_scores(f32x16 &sc, float d) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] *= d;
+}
+
 // Returns true (wave-uniform) when some row of this wave needs a re-run.
 //   scale_log2 > 0 (softmax_scale * log2 e, clamped away from 0 by the caller);
 //   mask: some key of this page may be invisible to some row of the wave.
@@ -368,7 +374,7 @@ template <bool kFp8, bool kSplit>
 __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
                                             f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
                                             int lane, int key0, int nvis, float scale_log2, bool mask,
-                                            const NextPage &nx) {
+                                            const LDS_AS float *desc, bool descale, const NextPage &nx) {
   const int hl = lane >> 5;
   const int r = lane & 31;
 
@@ -445,7 +451,8 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // tokens (i/4)*8 + 4*hl + i%4 (s[i]) of the tile.  Tiles are independent:
   // O and l share the fixed reference m, so nothing is rescaled; the first
   // tile with a visible key fixes m.
-  //   pieces 0-1: mask the scores of invisible keys (8 each)
+  //   pieces 0-1: mask the scores of invisible keys (8 each); piece 0 first
+  //               multiplies the row's scores by its qkDescale, if any
   //   pieces 2-5: running max over 4 scores each
   //   piece 6   : max across the lane halves, reference update, re-run flag
   //   pieces 7-14: probabilities exp2(s * scale_log2 - m), 2 each, and their sum
@@ -455,6 +462,7 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   bool need = false;
   auto soft = [&](f32x16 &sc, bf16x8 &p_lo, bf16x8 &p_hi, int tok0, int piece) {
     if (piece < 2) {
+      if (piece == 0 && descale) scale_scores(sc, desc[r]);
       if (mask) {
 #pragma unroll
         for (int i = 8 * piece; i < 8 * piece + 8; ++i) {
@@ -671,7 +679,7 @@ template <bool kSplit>
 __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i32x8 (&q8)[18], int s_hi, int s_lo,
                                                f32x16 (&o)[kOTiles], float &m, float &l, float &lq, float &m_restart,
                                                int lane, int key0, int nvis, float scale_log2, bool mask,
-                                               const NextPage &nx) {
+                                               const LDS_AS float *desc, bool descale, const NextPage &nx) {
   const int hl = lane >> 5;
   const int r = lane & 31;
   const int k127 = 127;                            // scale 1 for the cache codes
@@ -721,6 +729,7 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
   u32x4 p8[2];
   auto soft = [&](f32x16 &sc, int tile, int tok0, int piece) {
     if (piece < 2) {
+      if (piece == 0 && descale) scale_scores(sc, desc[r]);
       if (mask) {
 #pragma unroll
         for (int i = 8 * piece; i < 8 * piece + 8; ++i) {
@@ -934,12 +943,26 @@ __device__ __forceinline__ int xcd_part(int w, int n) {
   return x * q + min(x, r) + i;
 }
 
-// True when a device-held bmm1 scale is NaN, negative or infinite (the host
-// rejects such values for the host-side scale).
+// A device-held scale must be finite and >= 0 (the host rejects other
+// values of the host-side scale).
+__device__ __forceinline__ bool bad_value(float v) { return !(v >= 0.f && v < __builtin_inff()); }
+// True when a device-held bmm1 scale (plain or log2 form) is NaN, negative or
+// infinite (workgroup-uniform).
 __device__ __forceinline__ bool bad_device_scale(const DecodeArgs &a) {
-  if (!a.bmm1_dev) return false;
-  const float v = *a.bmm1_dev;
-  return !(v >= 0.f && v < __builtin_inff());
+  return a.bmm1_log2_dev ? bad_value(*a.bmm1_log2_dev) : a.bmm1_dev && bad_value(*a.bmm1_dev);
+}
+// Factor on q.k in base 2: the device log2 form, else the device bmm1, else
+// the host scale (workgroup-uniform).  A per-head qkDescale multiplies the
+// scores themselves.  Clamped away from 0 (the reference-max logic
+// multiplies -inf by it).
+__device__ __forceinline__ float scores_scale_log2(const DecodeArgs &a) {
+  const float s = a.bmm1_log2_dev ? *a.bmm1_log2_dev : a.bmm1_dev ? *a.bmm1_dev * kLog2e : a.scale_log2;
+  return fmaxf(s, 1e-30f);
+}
+// Factor on head h's output: bmm2 (device or host) times its pvDescale.
+__device__ __forceinline__ float row_v_scale(const DecodeArgs &a, int h) {
+  const float v = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
+  return a.pv_descale ? v * a.pv_descale[h] : v;
 }
 
 // kAnyBlock: the cache's block size is a.page_size (a multiple of 16) rather
@@ -975,7 +998,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   // bmm1_scale / bmm2_scale may be device tensors).  It cannot be validated
   // on the host: a NaN, negative or infinite value makes every output NaN.
   const bool bad_scale = bad_device_scale(a);
-  const float scale_log2 = fmaxf(a.bmm1_dev ? *a.bmm1_dev * kLog2e : a.scale_log2, 1e-30f);
+  const float scale_log2 = scores_scale_log2(a);
+  // Per-head qkDescale (Ascend ATB MLA page): each row's factor sits in LDS,
+  // 32 per wave, and multiplies its raw scores in the softmax; rows keep their
+  // head for the whole kernel.
+  LDS_AS float *const desc_tab = (LDS_AS float *)(smem + 2 * kPageBytes + 16) + wave * 32;
+  // The output factor of each row: bmm2 (device or host) times its head's
+  // pvDescale, read once per split in the epilogue.
+  LDS_AS float *const vfac_tab = desc_tab + kRowsPerTile;
+  if (active && lane < 32) {
+    const int h = row_coord(wrow0, a.rows, a.group, hk).h;
+    if (a.qk_descale) desc_tab[lane] = a.qk_descale[h];
+    vfac_tab[lane] = row_v_scale(a, h);
+  }
+  const bool descale = a.qk_descale != nullptr;
 
   const int elem = kFp8 ? 1 : 2;
   constexpr int kRowDim = kSplit ? kHeadDimV : kHeadDim;   // columns of a kv_cache row
@@ -1022,6 +1058,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const RowCoord c = row_coord(wrow0, a.rows, a.group, hk);
     const long r = ((long)min(b, a.batch - 1) * a.s_q + c.qi) * a.hq + c.h;
     if constexpr (kFp8) {
+      if (a.q_fp8) {
+        // An e4m3 query (its q_scale folded into bmm1; the host admits it
+        // with an fp8 cache only): the codes are the hi term as they are,
+        // with a zero lo term and unit scales.
+        const int hl = lane_id_here() >> 5;
+        const uint8_t *qc = (const uint8_t *)a.q + r * kHeadDim;
+#pragma unroll
+        for (int kb = 0; kb < 9; ++kb) {
+          const u32x4 x = *(const u32x4 *)(qc + 64 * kb + 16 * hl);
+          const u32x4 y = *(const u32x4 *)(qc + 64 * kb + 32 + 16 * hl);
+          q8[2 * kb] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+          q8[2 * kb + 1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        return;
+      }
       const int hl = lane_id_here() >> 5;
       const uint16_t *qn = a.q + r * a.q_stride;
       const uint16_t *qr = a.q_rope ? a.q_rope + r * (kHeadDim - kHeadDimV) : qn + kHeadDimV;
@@ -1070,8 +1121,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int hi0 = seq_end(b0, nblk0);
     // (a): the tile's 4 x 32 rows are whole 32-row runs of consecutive q rows
     // (no split q), and their 4 x 36 KiB fill both page buffers exactly.
-    const bool staged = a.q_rope == nullptr && a.group % 32 == 0 && (rt + 1) * kRowsPerTile <= a.rows &&
-                        a.q_stride == kHeadDim && hi0 > first0;   // workgroup-uniform
+    const bool staged = a.q_rope == nullptr && !a.q_fp8 && a.group % 32 == 0 &&
+                        (rt + 1) * kRowsPerTile <= a.rows && a.q_stride == kHeadDim && hi0 > first0;   // workgroup-uniform
     if (staged) {
       const int qi = wrow0 / a.group, h0 = hk * a.group + wrow0 % a.group;
       const uint8_t *qblock = (const uint8_t *)(a.q + (((long)b0 * a.s_q + qi) * a.hq + h0) * kHeadDim);
@@ -1161,7 +1212,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         const int t = slice_tok(j);
         return src_of(block_of(min(t / bs, nent - 1)), t % bs);
       };
-      if constexpr (kFp8) quantize_q_f8(q8, s_hi, s_lo);
+      if constexpr (kFp8) {
+        if (a.q_fp8) {
+          s_hi = s_lo = 127;                        // codes as loaded, lo term zero
+        } else {
+          quantize_q_f8(q8, s_hi, s_lo);
+        }
+      }
       for (int pass = 0;; ++pass) {
         bool need = false;
         if (!have_first) {
@@ -1189,10 +1246,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           if (active) {
             if constexpr (kFp8)
               need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
-                                             scale_log2, (j + 1) * kPage > nvis_min, nx);
+                                             scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
             else
               need |= attend_page<false, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
-                                                 (j + 1) * kPage > nvis_min, nx);
+                                                 (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
           } else if (nx.valid) {                    // a wave without rows still copies its share
             if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
             else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
@@ -1243,14 +1300,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         // normalise by their sum (scaled to lt) so that they add up to one.
         inv = kFp8 ? (lq > 0.f ? l * am / (lt * lq) : 0.f) : am / lt;
       }
-      if (bad_scale) inv = __builtin_nanf("");
-      const float lse_v = bad_scale ? __builtin_nanf("") : lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
+      const bool bad = bad_scale || (descale && bad_value(desc_tab[lane & 31]));
+      if (bad) inv = __builtin_nanf("");
+      const float lse_v = bad ? __builtin_nanf("") : lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
-      const float v_scale = a.bmm2_dev ? *a.bmm2_dev : a.v_scale;
       const int rows_pad = (a.rows + kPartRows - 1) / kPartRows * kPartRows;
-      if (direct)
-        store_rows(o, inv * v_scale, a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
+      if (direct && a.pv_descale)
+        store_rows(o, inv * vfac_tab[lane & 31], a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
+      else if (direct)
+        store_rows(o, inv * (a.bmm2_dev ? *a.bmm2_dev : a.v_scale), a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
       else
         store_acc_block(o, inv, a.part_o + ((long)(slot * a.hk + hk) * rows_pad + wrow0) * kHeadDimV);
       if (lane_id_here() < 32 && c.row < a.rows) {
@@ -1420,8 +1479,8 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
     const float zero[kSlots][8] = {};
     fold_state(mu, Z, acc, a.sinks[h], 1.f, zero);
   }
-  const bool bad_scale = bad_device_scale(a);
-  const float inv = bad_scale ? __builtin_nanf("") : Z > 0.f ? (a.bmm2_dev ? *a.bmm2_dev : a.v_scale) / Z : 0.f;
+  const bool bad_scale = bad_device_scale(a) || (a.qk_descale && bad_value(a.qk_descale[h]));
+  const float inv = bad_scale ? __builtin_nanf("") : Z > 0.f ? row_v_scale(a, h) / Z : 0.f;
   // Slot j of the unit is chunk slot 2t + pp = kSlots g + j: this lane
   // holds dims 32t + 16pp + 4hl + {0..3} (acc[j][0..3]) and + 8 (acc[j][4..7]).
   // v_permlane32_swap with lane ^ 32 forms whole 16-byte chunks: lanes < 32
@@ -1446,7 +1505,8 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  const size_t smem = 2 * (size_t)kPageBytes + 16;   // two pages (bf16 size) + restart flag
+  // Two pages (bf16 size), the restart flag, per-row qkDescale and output factors.
+  const size_t smem = 2 * (size_t)kPageBytes + 16 + 2 * kRowsPerTile * 4;
   const dim3 grid(a.num_parts, a.row_tiles * a.hk);   // one persistent workgroup per part
   auto launch = [&](auto kernel) -> hipError_t {
     hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

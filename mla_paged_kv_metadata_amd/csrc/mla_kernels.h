@@ -37,6 +37,10 @@ struct DecodeArgs {
   const float *sinks;         // nullptr, or fp32 [Hq] per-head sink logits
   const float *bmm1_dev;      // nullptr, or fp32 [1] replacing softmax_scale
   const float *bmm2_dev;      // nullptr, or fp32 [1] replacing v_scale
+  const float *bmm1_log2_dev; // nullptr, or fp32 [1]: bmm1 * log2(e), replacing softmax_scale and bmm1_dev
+  const float *qk_descale;    // nullptr, or fp32 [Hq]: per-head factor on the scores
+  const float *pv_descale;    // nullptr, or fp32 [Hq]: per-head factor on the output
+  int q_fp8;                  // q holds e4m3fn codes [B][s_q][Hq][576] (q_scale folded into bmm1)
 };
 
 hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int fixed_cost,

@@ -138,6 +138,37 @@ def test_ext_applies_the_plain_checks():
     assert _decode_ext(lib, ext, wsb=16) == 3
 
 
+@pytest.mark.parametrize("q_dtype,dt,q_rope,status", [
+    (2, 1, None, 2),        # unknown q dtype
+    (-1, 0, None, 2),
+    (1, 0, None, 2),        # fp8 q with a bf16 cache
+    (1, 1, 1, 2),           # fp8 q with a split query
+])
+def test_ext_rejects_unsupported_query_forms_before_any_device_call(q_dtype, dt, q_rope, status):
+    ext = mla.DecodeExt(None, None, None, None, q_rope, 0, None, None, None, q_dtype)
+    assert _decode_ext(mla.load_library(), ext, dt=dt) == status
+
+
+def test_python_wrapper_checks_descale_and_fp8_query_forms():
+    import torch
+    q = torch.zeros((1, 1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 64, 1, 576), dtype=torch.float8_e4m3fn)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    sl = torch.zeros((1,), dtype=torch.int32)
+    md = torch.zeros((4, 8), dtype=torch.int32)
+    ns = torch.zeros((2,), dtype=torch.int32)
+    with pytest.raises(ValueError):      # one factor per query head
+        mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, qk_descale=torch.ones(8))
+    with pytest.raises(TypeError):       # fp32 factors
+        mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, pv_descale=torch.ones(16, dtype=torch.float64))
+    with pytest.raises(ValueError):      # one base-2 scale
+        mla.mla_decode_fwd(q, kv, bt, sl, 512, md, ns, bmm1_scale_log2_tensor=torch.ones(2))
+    q8 = torch.zeros((1, 1, 16, 512), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError):      # an fp8 query is joined
+        mla.mla_decode_fwd(q8, kv[..., :512].contiguous(), bt, sl, 512, md, ns,
+                           q_rope=torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16))
+
+
 def test_python_wrapper_checks_split_layout_shapes():
     import torch
     q = torch.zeros((1, 1, 16, 576), dtype=torch.bfloat16)

@@ -8,6 +8,7 @@ from .mla_inputs import (  # noqa: F401
     CONFIGS,
     Workload,
     bf16_bits_from_f32,
+    fp8_query,
     make_config,
     make_workload,
     repage,

@@ -107,6 +107,14 @@ class Workload:
         return (L + self.page_block_size - 1) // self.page_block_size
 
 
+def fp8_query(w: "Workload", seed: int):
+    """An e4m3fn query of the workload's q shape: N(0, 1) draws quantised with
+    one per-tensor scale (as the fp8 cache).  Returns (codes uint8, q_scale)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes, q_scale = _normal_e4m3fn(rng, int(np.prod(w.q_bits.shape)))
+    return codes.reshape(w.q_bits.shape), q_scale
+
+
 def _page_pool(rng, seqlens, num_heads_k, extra_pages=0, padding="zero", page=PAGE):
     """Shuffled page pool: pages assigned b-major from one random permutation."""
     nblk = [(int(L) + page - 1) // page for L in seqlens]
