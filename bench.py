@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 ctx~4K"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(*a):
@@ -51,7 +52,17 @@ def work_counts(w):
 
 
 DECODE_SOURCES = ["mla_paged_kv_metadata_amd/csrc/mla_decode.hip", "mla_paged_kv_metadata_amd/csrc/mla_kernels.h"]
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_c2_hbm_traffic.json")
+
+
+def traffic_json(cfg):
+    return os.path.join(ROOT, "profiles", f"decode_c{cfg}_hbm_traffic.json")
+
+
+WORKLOAD_NAMES = {1: "tiny MLA decode: B=2 s_q=1 H_q=16 L={127,300}",
+                  2: "standard MLA decode: B=64 s_q=1 H_q=128 L~U[1024,4096]",
+                  3: "MTP causal MLA decode: B=128 s_q=2 H_q=128 L~U[2048,8192]",
+                  4: "skewed MLA decode: B=32 s_q=1 H_q=16, one 65536 + 31 lognormal(512,1) lengths",
+                  5: "fp8-e4m3 KV MLA decode: B=128 s_q=1 H_q=128 L=8192"}
 
 
 def decode_source_hash():
@@ -63,14 +74,15 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when the decode kernel's sources changed since the counters were taken."""
+def measured_traffic(cfg):
+    """HBM bytes per mla_decode_fwd call (split attention + combine) from the
+    committed counter summary of the workload, or None when the kernels'
+    sources changed since the counters were taken."""
     try:
-        with open(TRAFFIC_JSON) as fh:
+        with open(traffic_json(cfg)) as fh:
             rec = json.load(fh)
         if rec.get("decode_source_hash") == decode_source_hash():
-            return int(rec["hbm_bytes_per_launch"])
+            return int(rec["hbm_bytes_per_call"])
     except (OSError, ValueError, KeyError):
         pass
     return None
@@ -101,40 +113,74 @@ def _per_dispatch(rows, counter, name_part):
     return sum(per.values()) / len(per), len(per)
 
 
-def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, commands):
-    """Writes profiles/decode_c2_hbm_traffic.{md,json} from four rocprofv3 --pmc runs."""
+def pmc_summary(cfg, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, commands, lds_fetch_dir=None):
+    """Writes profiles/decode_c<cfg>_hbm_traffic.{md,json} from rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of the bench workload (split-attention and
+    combine kernels), and of the calibration reads of copy_mib MiB: a plain
+    device copy and, if given, the LDS-DMA read (mla_lds_dma_read)."""
     copy_bytes = copy_mib << 20
     cf, _ = _per_dispatch(_counter_rows(copy_fetch_dir), "FETCH_SIZE", "copy")
     cw, _ = _per_dispatch(_counter_rows(copy_write_dir), "WRITE_SIZE", "copy")
-    df, nf = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE", "mla_decode_kernel")
-    dw, nw = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE", "mla_decode_kernel")
     kf, kw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    fetch_b, write_b = df * 1024 * kf, dw * 1024 * kw
+    lf = kl = None
+    if lds_fetch_dir:
+        lf, _ = _per_dispatch(_counter_rows(lds_fetch_dir), "FETCH_SIZE", "lds_dma_read")
+        kl = copy_bytes / (lf * 1024)
+    frows, wrows = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    df, nf = _per_dispatch(frows, "FETCH_SIZE", "mla_decode_kernel")
+    dw, nw = _per_dispatch(wrows, "WRITE_SIZE", "mla_decode_kernel")
+    try:
+        cbf, _ = _per_dispatch(frows, "FETCH_SIZE", "mla_combine_kernel")
+        cbw, _ = _per_dispatch(wrows, "WRITE_SIZE", "mla_combine_kernel")
+    except SystemExit:                 # no split sequences: no combine launch
+        cbf = cbw = 0.0
+    # The page copies are LDS-DMA reads: the decode's fetch is scaled by the
+    # LDS-DMA calibration when there is one; the combine's plain loads by the copy's.
+    dec_fetch = df * 1024 * (kl if kl else kf)
+    dec_write = dw * 1024 * kw
+    cmb_fetch, cmb_write = cbf * 1024 * kf, cbw * 1024 * kw
     from workloads import make_config
-    w = make_config(2)
+    w = make_config(cfg)
     _, kv_bytes, alg_bytes = work_counts(w)
-    rec = {"kernel": "mla_decode_kernel<bf16>", "workload": "standard MLA decode B=64 H=128 L~U[1024,4096]",
+    kname = f"mla_decode_kernel<{'fp8' if w.kv_dtype == 'fp8_e4m3fn' else 'bf16'}>"
+    rec = {"kernels": [kname, "mla_combine_kernel"], "workload": WORKLOAD_NAMES[cfg],
            "decode_source_hash": decode_source_hash(),
-           "fetch_kib_per_dispatch": round(df, 1), "write_kib_per_dispatch": round(dw, 1),
+           "decode_fetch_kib_per_dispatch": round(df, 1), "decode_write_kib_per_dispatch": round(dw, 1),
+           "combine_fetch_kib_per_dispatch": round(cbf, 1), "combine_write_kib_per_dispatch": round(cbw, 1),
            "copy_mib": copy_mib, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
            "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
-           "hbm_bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "lds_dma_fetch_kib": None if lf is None else round(lf, 1),
+           "lds_dma_fetch_factor": None if kl is None else round(kl, 4),
+           "decode_fetch_bytes": int(dec_fetch), "decode_write_bytes": int(dec_write),
+           "combine_fetch_bytes": int(cmb_fetch), "combine_write_bytes": int(cmb_write),
+           "hbm_bytes_per_launch": int(dec_fetch + dec_write),
+           "hbm_bytes_per_call": int(dec_fetch + dec_write + cmb_fetch + cmb_write),
            "algorithmic_bytes_per_launch": alg_bytes, "kv_bytes_per_launch": kv_bytes,
            "dispatches": {"fetch": nf, "write": nw}, "commands": commands}
-    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
-    with open(TRAFFIC_JSON, "w") as fh:
+    path = traffic_json(cfg)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
-    md = TRAFFIC_JSON[:-5] + ".md"
+    md = path[:-5] + ".md"
     with open(md, "w") as fh:
-        fh.write("# HBM traffic of mla_decode_kernel<bf16>, standard decode B=64 H=128 L~U[1024,4096]\n\n")
-        fh.write("rocprofv3 TCC counters per dispatch (KiB, summed over instances), scaled by a plain "
-                 f"{copy_mib} MiB device copy measured the same way.\n\n")
+        fh.write(f"# HBM traffic of mla_decode_fwd ({kname} + mla_combine_kernel), {WORKLOAD_NAMES[cfg]}\n\n")
+        fh.write("rocprofv3 TCC counters per dispatch (KiB, summed over instances), each scaled by what the "
+                 f"same counter reads for a calibration of known size ({copy_mib} MiB): a plain device copy "
+                 "for plain loads and stores"
+                 + (", and a read through the page copies' LDS-DMA instruction (mla_lds_dma_read) for the "
+                    "split-attention kernel's fetch" if kl else "") + ".\n\n")
         fh.write("| quantity | value |\n|---|---|\n")
-        for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_kib", "copy_write_kib",
-                  "fetch_factor", "write_factor", "fetch_bytes", "write_bytes", "hbm_bytes_per_launch",
-                  "algorithmic_bytes_per_launch", "kv_bytes_per_launch", "decode_source_hash"):
+        for k in ("decode_fetch_kib_per_dispatch", "decode_write_kib_per_dispatch", "combine_fetch_kib_per_dispatch",
+                  "combine_write_kib_per_dispatch", "copy_fetch_kib", "copy_write_kib", "fetch_factor",
+                  "write_factor", "lds_dma_fetch_kib", "lds_dma_fetch_factor", "decode_fetch_bytes",
+                  "decode_write_bytes", "combine_fetch_bytes", "combine_write_bytes", "hbm_bytes_per_launch",
+                  "hbm_bytes_per_call", "algorithmic_bytes_per_launch", "kv_bytes_per_launch",
+                  "decode_source_hash"):
             fh.write(f"| {k} | {rec[k]} |\n")
-        fh.write(f"\nmeasured / algorithmic bytes: {rec['hbm_bytes_per_launch'] / alg_bytes:.3f}\n\n")
+        fh.write(f"\nsplit-attention kernel, measured / algorithmic bytes: "
+                 f"{rec['hbm_bytes_per_launch'] / alg_bytes:.3f}\n")
+        fh.write(f"whole call (split attention + combine), measured / algorithmic bytes: "
+                 f"{rec['hbm_bytes_per_call'] / alg_bytes:.3f}\n\n")
         fh.write("Commands (from the repository root):\n\n")
         for c in commands:
             fh.write(f"    {c}\n")
@@ -153,8 +199,8 @@ def _per_dispatch_max(rows, counter, name_part):
     return sum(per.values()) / len(per), len(per)
 
 
-def mfma_summary(counter_dir, commands, simds=1024, xcds=8):
-    """Writes profiles/decode_c2_mfma_lds.md from one rocprofv3 --pmc run of the
+def mfma_summary(cfg, counter_dir, commands, simds=1024, xcds=8):
+    """Writes profiles/decode_c<cfg>_mfma_lds.md from one rocprofv3 --pmc run of the
     matrix-core and LDS counters.  MFMA utilisation is the MFMA busy cycles per
     SIMD over the GPU-active cycles of one XCD: GRBM_GUI_ACTIVE comes back as one
     instance that adds up the 8 XCDs (its value / 8 matches the kernel's duration
@@ -163,29 +209,35 @@ def mfma_summary(counter_dir, commands, simds=1024, xcds=8):
     k = "mla_decode_kernel"
     busy, n = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", k)
     gui, _ = _per_dispatch_max(rows, "GRBM_GUI_ACTIVE", k)
-    mops, _ = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16", k)
+    from workloads import make_config
+    w = make_config(cfg)
+    fp8 = w.kv_dtype == "fp8_e4m3fn"
+    # bf16: MOPS (units of 512 FLOPs); fp8: instructions, every one of them a
+    # 32x32x64 MFMA (131072 FLOPs), as there is no fp8 MOPS counter.
+    mops_name = "SQ_INSTS_VALU_MFMA_F8" if fp8 else "SQ_INSTS_VALU_MFMA_MOPS_BF16"
+    flops_per = 32 * 32 * 64 * 2 if fp8 else 512
+    mops, _ = _per_dispatch(rows, mops_name, k)
     conf, _ = _per_dispatch(rows, "SQ_LDS_BANK_CONFLICT", k)
     lds_act, _ = _per_dispatch(rows, "SQ_LDS_IDX_ACTIVE", k)
     lds_ins, _ = _per_dispatch(rows, "SQ_INSTS_LDS", k)
-    from workloads import make_config
-    w = make_config(2)
     alg_flops, _, _ = work_counts(w)
     util = 100.0 * (busy / simds) / (gui / xcds)
-    md = os.path.join(ROOT, "profiles", "decode_c2_mfma_lds.md")
+    md = os.path.join(ROOT, "profiles", f"decode_c{cfg}_mfma_lds.md")
+    kname = f"mla_decode_kernel<{'fp8' if fp8 else 'bf16'}>"
     with open(md, "w") as fh:
-        fh.write("# Matrix-core and LDS counters of mla_decode_kernel<bf16>, standard decode B=64 H=128 "
-                 "L~U[1024,4096]\n\n")
+        fh.write(f"# Matrix-core and LDS counters of {kname}, {WORKLOAD_NAMES[cfg]}\n\n")
         fh.write(f"rocprofv3 SQ/GRBM counters, averaged over {n} dispatches (one value per counter and "
                  "dispatch as rocprofv3 reports it).\n\n")
         fh.write("| quantity | value |\n|---|---|\n")
         for name, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", gui),
-                        ("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), ("SQ_LDS_BANK_CONFLICT", conf),
+                        (mops_name, mops), ("SQ_LDS_BANK_CONFLICT", conf),
                         ("SQ_LDS_IDX_ACTIVE", lds_act), ("SQ_INSTS_LDS", lds_ins)):
             fh.write(f"| {name} | {v:.0f} |\n")
         fh.write(f"| MFMA busy cycles per SIMD (busy / {simds}) | {busy / simds:.0f} |\n")
         fh.write(f"| GPU-active cycles per XCD (GRBM_GUI_ACTIVE / {xcds}) | {gui / xcds:.0f} |\n")
         fh.write(f"| MFMA utilisation (per-SIMD busy / per-XCD active) | {util:.1f}% |\n")
-        fh.write(f"| bf16 MFMA FLOPs per dispatch (MOPS x 512) | {mops * 512 / 1e9:.2f} G |\n")
+        fh.write(f"| {'fp8' if fp8 else 'bf16'} MFMA FLOPs per dispatch ({'instructions x 131072' if fp8 else 'MOPS x 512'})"
+                 f" | {mops * flops_per / 1e9:.2f} G |\n")
         fh.write(f"| algorithmic FLOPs per dispatch | {alg_flops / 1e9:.2f} G |\n")
         fh.write(f"| LDS bank-conflict cycles / LDS active cycles | {conf / max(lds_act, 1):.3f} |\n")
         fh.write("\nCommands (from the repository root):\n\n")
@@ -194,8 +246,8 @@ def mfma_summary(counter_dir, commands, simds=1024, xcds=8):
     print(open(md).read())
 
 
-def trace_summary(trace_dir, commands, bench_json=None):
-    """Writes profiles/decode_c2_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder
+def trace_summary(cfg, trace_dir, commands, bench_json=None):
+    """Writes profiles/decode_c<cfg>_kernel_trace.md from a rocprofv3 --kernel-trace --stats folder
     (and, if given, the JSON line that the profiled bench run printed)."""
     import csv
     import glob
@@ -203,9 +255,9 @@ def trace_summary(trace_dir, commands, bench_json=None):
     if not f:
         raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
     rows = list(csv.DictReader(open(f[0], newline="")))
-    md = os.path.join(ROOT, "profiles", "decode_c2_kernel_trace.md")
+    md = os.path.join(ROOT, "profiles", f"decode_c{cfg}_kernel_trace.md")
     with open(md, "w") as fh:
-        fh.write("# rocprofv3 kernel trace, standard decode B=64 H=128 L~U[1024,4096] (bench.py workload)\n\n")
+        fh.write(f"# rocprofv3 kernel trace, {WORKLOAD_NAMES[cfg]} (bench.py workload)\n\n")
         fh.write("| kernel | calls | average us | min us | max us | share |\n|---|---|---|---|---|---|\n")
         for r in rows:
             name = r["Name"]
@@ -302,11 +354,14 @@ def main():
                     help="tokens per cache block (a multiple of 16); the same rows re-laid in blocks of this size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--lds-dma-calibration", type=int, default=0, metavar="MIB",
+                    help="only read this many MiB through the page copies' LDS-DMA instruction (counter calibration)")
+    ap.add_argument("--lds-dma-fetch-dir", help="with --pmc-summary: FETCH_SIZE folder of an --lds-dma-calibration run")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise four rocprofv3 --pmc output folders into profiles/ (no GPU work)")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy for --pmc-summary")
     ap.add_argument("--mfma-summary", metavar="COUNTER_DIR",
-                    help="write profiles/decode_c2_mfma_lds.md from a rocprofv3 --pmc run of the MFMA/LDS counters")
+                    help="write profiles/decode_c<config>_mfma_lds.md from a rocprofv3 --pmc run of the MFMA/LDS counters")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats folder into profiles/ (no GPU work)")
     ap.add_argument("--bench-json", help="the profiled run's JSON line, quoted in a --trace-summary file")
@@ -314,13 +369,13 @@ def main():
                     help="command line recorded in a --pmc-summary / --trace-summary file")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, args.copy_mib, args.pmc_command)
+        pmc_summary(args.config, *args.pmc_summary, args.copy_mib, args.pmc_command, args.lds_dma_fetch_dir)
         return
     if args.mfma_summary:
-        mfma_summary(args.mfma_summary, args.pmc_command)
+        mfma_summary(args.config, args.mfma_summary, args.pmc_command)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.pmc_command, args.bench_json)
+        trace_summary(args.config, args.trace_summary, args.pmc_command, args.bench_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this decode path is built and "
@@ -340,6 +395,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {n} bytes 3 times")
+        return
+    if args.lds_dma_calibration:
+        n = args.lds_dma_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        for _ in range(3):
+            mla.lds_dma_read(src)
+        torch.cuda.synchronize()
+        log(f"read {n} bytes through LDS-DMA 3 times")
         return
     mla.load_library()
     dev = torch.device("cuda:0")
@@ -561,40 +624,41 @@ def main():
     fwd_s = fwd_med * 1e-6
     dec_s = t_dec_us * 1e-6
     # Rooflines of the shape: HBM bytes at 8 TB/s; the matrix-core peak of the
-    # arithmetic the kernels run (bf16 MFMA, also for an fp8 cache whose codes
-    # are widened to bf16 operands).  The graded fraction is over the whole
-    # mla_decode_fwd call (split attention + combine).
+    # arithmetic the kernels run (bf16 MFMA for a bf16 cache, fp8 MFMA for an
+    # e4m3 cache, whose codes enter the fp8 matrix core as they are).  The
+    # graded fraction is over the whole mla_decode_fwd call (split attention +
+    # combine).
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
     t_bf16 = flops / (BF16_PEAK_TFLOPS * 1e12)
-    mfma_bound = t_bf16 > t_hbm
+    t_fp8 = flops / (FP8_PEAK_TFLOPS * 1e12)
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+    t_mfma = t_fp8 if fp8 else t_bf16
+    mfma_bound = t_mfma > t_hbm
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(flops / fwd_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(t_bf16 / fwd_s, 4)}
+        roof = {"bound": "mfma", "achieved": round(flops / fwd_s / 1e12, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(t_mfma / fwd_s, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(alg_bytes / fwd_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(t_hbm / fwd_s, 4)}
     plain = not (args.sinks or args.split_cache or args.device_scales) and w.page_block_size == 64
     roof.update({
-        "traffic": measured_traffic() if args.config == 2 and plain else None,
+        "traffic": measured_traffic(args.config) if plain else None,
         "timed": "mla_decode_fwd (split attention + combine), HIP events per call, cold caches",
         "t_median_us": round(fwd_med, 2), "t_min_us": round(fwd_min, 2), "iterations": len(fwd),
-        "frac_at_min": round(max(t_hbm, t_bf16) / (fwd_min * 1e-6), 4),
-        "back_to_back": {"us": round(warm_us, 2), "frac": round(max(t_hbm, t_bf16) / (warm_us * 1e-6), 4),
+        "frac_at_min": round(max(t_hbm, t_mfma) / (fwd_min * 1e-6), 4),
+        "back_to_back": {"us": round(warm_us, 2), "frac": round(max(t_hbm, t_mfma) / (warm_us * 1e-6), 4),
                          "timed": "decode and combine kernels, each as K launches back to back in a graph"},
         "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": flops,
         "hbm_frac": round(t_hbm / fwd_s, 4), "bf16_mfma_frac": round(t_bf16 / fwd_s, 4),
-        "roofline_us": {"hbm_8tbs": round(t_hbm * 1e6, 2), "bf16_mfma": round(t_bf16 * 1e6, 2)},
+        **({"fp8_mfma_frac": round(t_fp8 / fwd_s, 4)} if fp8 else {}),
+        "roofline_us": {"hbm_8tbs": round(t_hbm * 1e6, 2), "bf16_mfma": round(t_bf16 * 1e6, 2),
+                        **({"fp8_mfma": round(t_fp8 * 1e6, 2)} if fp8 else {})},
         "decode_only": {"kernel": f"mla_decode_kernel<{'fp8' if fp8 else 'bf16'}>", "avg_us": round(t_dec_us, 2),
-                        "frac": round(max(t_hbm, t_bf16) / dec_s, 4)},
+                        "frac": round(max(t_hbm, t_mfma) / dec_s, 4)},
         "copy_gbps_measured": round(copy_gbps, 1),
         "copy_kind": "1 GiB device-to-device copy, read + write bytes, best of 5",
     })
-    names = {1: "tiny MLA decode: B=2 s_q=1 H_q=16 L={127,300}",
-             2: "standard MLA decode: B=64 s_q=1 H_q=128 L~U[1024,4096]",
-             3: "MTP causal MLA decode: B=128 s_q=2 H_q=128 L~U[2048,8192]",
-             4: "skewed MLA decode: B=32 s_q=1 H_q=16, one 65536 + 31 lognormal(512,1) lengths",
-             5: "fp8-e4m3 KV MLA decode: B=128 s_q=1 H_q=128 L=8192"}
-    desc = names[args.config] + f", H_k={w.num_heads_k} D=576 Dv=512 page={w.page_block_size} seed {args.config}"
+    desc = WORKLOAD_NAMES[args.config] + f", H_k={w.num_heads_k} D=576 Dv=512 page={w.page_block_size} seed {args.config}"
     desc += ", bf16 q ~0.5*N(0,1)" if args.config == 3 else ", bf16 q ~N(0,1)"
     if fp8:
         desc += f", e4m3fn cache (per-tensor scale {w.k_scale:.4g}), fused bmm1={s1:.4g} bmm2={s2:.4g}"
@@ -617,7 +681,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": desc,
                    "batch": w.batch, "seq_len_q": w.s_q, "num_heads_q": w.num_heads_q, "causal": bool(w.causal),

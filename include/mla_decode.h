@@ -296,6 +296,14 @@ int mla_decode_fwd_noalloc(const void *q, int batch, int s_q, int num_heads_q, i
                            const int32_t *tile_md, int num_parts, const int32_t *num_splits,
                            void *out, float *lse, void *stream);
 
+/* Measurement aid, not part of the decode: reads `bytes` (a positive
+ * multiple of 1024) of device memory at `src` into LDS with the same 16-byte
+ * LDS-DMA instruction and cache hint as the decode's page copies, and writes
+ * nothing.  Hardware counters of HBM traffic are calibrated against it: the
+ * bytes such a read fetches are known exactly.  INVALID_ARG for a NULL src
+ * or a bad size; the call is asynchronous on `stream`. */
+int mla_lds_dma_read(const void *src, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

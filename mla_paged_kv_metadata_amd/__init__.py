@@ -61,6 +61,8 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_fwd_ext.argtypes = _DECODE_ARGTYPES + [ctypes.POINTER(DecodeExt)]
     lib.mla_decode_fwd_noalloc.restype = _c_int
     lib.mla_decode_fwd_noalloc.argtypes = _DECODE_ARGTYPES[:20] + _DECODE_ARGTYPES[22:]
+    lib.mla_lds_dma_read.restype = _c_int
+    lib.mla_lds_dma_read.argtypes = [_vp, _c_size, _vp]
     _lib = lib
     return lib
 
@@ -383,3 +385,14 @@ def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v, t
 __all__ = ["load_library", "mla_num_parts", "mla_get_metadata", "mla_workspace_bytes", "mla_decode_fwd",
            "mla_decode_fwd_noalloc",
            "get_mla_metadata", "flash_mla_with_kvcache", "fp8_fused_scales", "MlaError", "LIB_PATH"]
+
+
+def lds_dma_read(src: torch.Tensor) -> None:
+    """Measurement aid (mla_lds_dma_read): reads the bytes of a contiguous
+    device tensor (a multiple of 1 KiB) into LDS with the page copies' LDS-DMA
+    instruction, for calibrating HBM traffic counters."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    n = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        _check(load_library().mla_lds_dma_read(_ptr(src), n, _stream(src.device)))

@@ -332,4 +332,14 @@ int mla_decode_fwd_noalloc(const void *q, int batch, int s_q, int num_heads_q, i
                      causal, tile_md, num_parts, num_splits, ws, MLA_NOALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
+int mla_lds_dma_read(const void *src, size_t bytes, void *stream) {
+  if (!src || bytes == 0 || bytes % 1024) return fail(MLA_ERR_INVALID_ARG, "src must be non-NULL and bytes a positive multiple of 1024");
+  DeviceInfo d;
+  int rc = current_device(&d);
+  if (rc) return rc;
+  hipError_t e = mla::launch_lds_dma_read(src, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // extern "C"

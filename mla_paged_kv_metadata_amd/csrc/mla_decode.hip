@@ -38,6 +38,7 @@
 //    The fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
 //    softmax_scale and v_scale.
 #include "mla_kernels.h"
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -1502,6 +1503,25 @@ __global__ __launch_bounds__(kCombineWays * 64) void mla_combine_kernel(const De
     a.lse[((long)b * a.hq + h) * a.s_q + qi] = bad_scale ? __builtin_nanf("") : Z > 0.f ? mu + __logf(Z) : kNegInf;
 }
 
+// Counter calibration: streams `chunks` KiB from src into LDS with the page
+// copies' instruction (global_load_lds_dwordx4 with the non-temporal hint),
+// 1 KiB per wave instruction, up to 8 in flight per wave.  Nothing is
+// written to global memory.
+__global__ __launch_bounds__(256) void lds_dma_read_kernel(const uint8_t *src, long chunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][8][1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const long stride = (long)gridDim.x * 4;
+  int slot = 0;
+  for (long c = (long)blockIdx.x * 4 + wave; c < chunks; c += stride) {
+    lds_dma16<0>(src + c * 1024 + lane * 16, (LDS_AS void *)&ring[wave][slot][0]);
+    if (++slot == 8) {
+      wait_vmcnt<0>();
+      slot = 0;
+    }
+  }
+  wait_vmcnt<0>();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
@@ -1562,6 +1582,13 @@ hipError_t noalloc_scratch(void **ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+hipError_t launch_lds_dma_read(const void *src, size_t bytes, hipStream_t stream) {
+  const long chunks = (long)(bytes / 1024);
+  const int grid = (int)std::min<long>(2048, std::max<long>(1, (chunks + 3) / 4));
+  hipLaunchKernelGGL(lds_dma_read_kernel, dim3(grid), dim3(256), 0, stream, (const uint8_t *)src, chunks);
+  return hipGetLastError();
 }
 
 }  // namespace mla

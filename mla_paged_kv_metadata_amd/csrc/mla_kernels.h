@@ -50,5 +50,8 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
 // Device address of the static scratch array on the current device (looked
 // up once per device).
 hipError_t noalloc_scratch(void **ptr);
+// Counter calibration: reads bytes (a multiple of 1 KiB) into LDS with the
+// page copies' LDS-DMA instruction.
+hipError_t launch_lds_dma_read(const void *src, size_t bytes, hipStream_t stream);
 
 }  // namespace mla

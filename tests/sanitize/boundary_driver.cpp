@@ -18,6 +18,7 @@ hipError_t launch_metadata(const int32_t *, int, int, int, int32_t *, int32_t *,
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_combine(const DecodeArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t noalloc_scratch(void **) { return hipErrorNotSupported; }
+hipError_t launch_lds_dma_read(const void *, size_t, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace mla
 
 namespace {

@@ -197,3 +197,11 @@ def test_noalloc_refuses_oversized_problems_before_any_device_call():
     # Invalid sizes are INVALID_ARG, as for mla_decode_fwd.
     assert lib.mla_decode_fwd_noalloc(P(1), 0, 1, 16, 576, P(1), 0, 8, 64, 1, P(1), 1, P(1), 512, 0.04, 1.0, 0,
                                       P(1), 4, P(1), P(1), P(1), P(0)) == 1
+
+
+def test_lds_dma_read_rejects_bad_sizes_before_any_device_call():
+    lib = mla.load_library()
+    P = ctypes.c_void_p
+    assert lib.mla_lds_dma_read(P(0), 1024, P(0)) == 1
+    assert lib.mla_lds_dma_read(P(1), 0, P(0)) == 1
+    assert lib.mla_lds_dma_read(P(1), 1000, P(0)) == 1

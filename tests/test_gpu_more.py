@@ -116,3 +116,14 @@ def test_invalid_device_bmm1_gives_nan(gpu_lib, bad, parts):
     out, lse = mla.mla_decode_fwd(q, kv, bt, sl, DV, md, ns, bmm1_scale_tensor=b1)
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
+
+
+def test_lds_dma_read_calibration_runs(gpu_lib):
+    """The counter-calibration read (mla_lds_dma_read) runs on sizes that do
+    and do not fill its grid, and refuses a size that is not whole KiB."""
+    for kib in (1, 3, 4096, 65536):
+        src = torch.ones(kib * 1024, dtype=torch.uint8, device="cuda")
+        mla.lds_dma_read(src)
+    torch.cuda.synchronize()
+    with pytest.raises(mla.MlaError):
+        mla.lds_dma_read(torch.ones(1000, dtype=torch.uint8, device="cuda"))
