@@ -574,6 +574,114 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   return __ballot(need) != 0;
 }
 
+// One 32-token tile (tokens 32 tile .. +31 of a bf16 page, key0 = the
+// tile's first token) for this wave's 32 rows: used when a workgroup has at
+// most 32 rows, so that two waves share each page (wave w takes tile w) and
+// each runs half the matrix-core work of attend_page.  The same scheme as
+// attend_page (reference max, re-run flag, P^T straight from the scores),
+// but the softmax cannot hide under another tile's products: scores (36
+// MFMAs, copying this wave's quarter of the next page every 2nd step),
+// softmax, then O^T += V^T P^T over the tile's two 16-token k-steps.  Tile 1
+// accumulates output tiles 8..15 in o[0..7] and 0..7 in o[8..15] (o[mt]
+// holds output tile mt ^ 8), so that both waves finish o[0..7] after the
+// merge.
+template <bool kSplit>
+__device__ __forceinline__ bool attend_tile(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
+                                            f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
+                                            int lane, int key0, int nvis, float scale_log2, bool mask,
+                                            const LDS_AS float *desc, bool descale, const NextPage &nx, int tile) {
+  const int hl = lane >> 5;
+  const int r = lane & 31;
+  // K of token r of the tile (see attend_page): four lane bases plus immediates.
+  const LDS_AS uint8_t *kb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) kb[v] = pg + tile * 4096 + r * 128 + ((2 * v + hl) ^ swz_h(r)) * 16;
+  // V^T as in attend_page, restricted to the tile's k-steps 2 tile, 2 tile + 1.
+  const int g = lane >> 4, s16 = lane & 15, rr = s16 >> 2, qd = s16 & 3;
+  const int xb = g >> 1, t1 = rr >> 1, y = 2 * (g & 1) + (qd >> 1);
+  const int la = (4 * xb + rr) * 128 + (y ^ (2 * xb)) * 16 + (qd & 1) * 8;
+  const int lb = (4 * xb + rr) * 128 + 1024 + (y ^ (2 * xb + 1)) * 16 + (qd & 1) * 8;
+  const LDS_AS uint8_t *pt = pg + 4096 * tile;
+  const LDS_AS uint8_t *va_even = pt + la + 64 * t1, *va_odd = pt + la + 64 * (1 - t1);
+  const LDS_AS uint8_t *vb_even = pt + lb + 64 * t1, *vb_odd = pt + lb + 64 * (1 - t1);
+  auto kload = [&](int ks) { return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2)); };
+  // Output tile mt ^ 8 tile for o[mt]: 32 KiB further on for mt < 8, back for mt >= 8.
+  const int vswap = 32768 * tile;
+  auto vload = [&](int step) {
+    const int ks = step >> 4, mt = step & 15;         // k-step of the tile, accumulator mt
+    const int ofs = 8192 * (mt >> 1) + 2048 * ks + (mt < 8 ? vswap : -vswap);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // Scores: one accumulation chain over the 36 k-steps, K operands 4 ahead.
+  constexpr int kPre = 4;
+  constexpr int kDmaEvery = kKSteps / kPageLoads;     // 2: this wave's 18 copy instructions
+  bf16x8 kf[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) kf[i] = kload(i);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 sc;
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    const int sl = ks % kPre;
+    if (ks == 0) mfma_qk_first(sc, kf[sl], qf[0]);
+    else mfma_qk(sc, kf[sl], qf[ks]);
+    if (ks + kPre < kKSteps) kf[sl] = kload(ks + kPre);
+    if (nx.valid && ks % kDmaEvery == 0) dma_bf16_dispatch<kSplit>(nx.src, nx.dst, nx.wave, ks / kDmaEvery);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // V^T operands of the first PV steps load while the softmax runs.
+  constexpr int kVPre = 3;
+  bf16x8 vraw[kVPre];
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) vraw[i] = vload(i);
+  mfma_qk_drain(sc);
+
+  // Softmax of the tile (as attend_page's pieces, in one run).  In S^T a lane
+  // holds head r and tokens (i/4)*8 + 4*hl + i%4 of the tile.
+  if (descale) scale_scores(sc, desc[r]);
+  if (mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = key0 + (i >> 2) * 8 + hl * 4 + (i & 3);
+      if (tok >= nvis) sc[i] = kNegInf;
+    }
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+  float t = max_across_halves(mx);
+  t = (t == kNegInf) ? kNegInf : t * scale_log2;
+  if (m == kNegInf) m = t;                            // first visible keys fix the reference
+  const bool need = t > m + kRefSlackLog2;
+  if (need) m_restart = fmaxf(m_restart, t);
+  const float mu = (m == kNegInf) ? 0.f : m;
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], scale_log2, -mu));
+    ps += sc[i];
+  }
+  bf16x8 pb[2];                                       // P^T for the tile's k-steps 0 and 1
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pb[0][e] = (__bf16)sc[e];
+    pb[1][e] = (__bf16)sc[8 + e];
+  }
+  l += sum_across_halves(ps);
+
+  // O^T += V^T P^T: 2 k-steps x 16 output tiles, V^T operands 3 ahead.
+#pragma unroll
+  for (int step = 0; step < 2 * kOTiles; ++step) {
+    const int sl = step % kVPre;
+    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vraw[sl], pb[step >> 4], o[step & 15], 0, 0, 0);
+    if (step + kVPre < 2 * kOTiles) vraw[sl] = vload(step + kVPre);
+  }
+  return __ballot(need) != 0;
+}
+
 // ---------------------------------------------------------------------------
 // fp8 (e4m3fn) cache on the fp8 matrix core: v_mfma_scale_f32_32x32x64_f8f6f4.
 //
@@ -888,28 +996,66 @@ __device__ __forceinline__ RowCoord row_coord(int wrow0, int rows, int group, in
 //   row_idx : this lane's destination row index in units of 512 elements
 //             (lanes l and l + 32 hold row l % 32 of the wave)
 //   nrows   : number of valid rows of the wave (0..32)
+// Output tiles of O^T as 8-value pieces (t, pp): o[t][8pp .. 8pp+7] times
+// f, for all 16 tiles, or (kMerge) for o[0 .. 7], which hold output tiles
+// 8 half .. 8 half + 7 (half wave-uniform, 0 or 1), plus f1 times the same
+// elements of a second state that another wave left in LDS at xb (f32x4 h
+// of piece i = 2t + pp of lane L at byte 16 ((2i + h) 64 + L)).  The second
+// state's values are read one piece ahead, so that the LDS latency overlaps
+// the previous piece's stores.  fn(output tile, pp, v) consumes each piece.
+template <bool kMerge, typename Fn>
+__device__ __forceinline__ void for_each_piece(const f32x16 (&o)[kOTiles], float f, const LDS_AS uint8_t *xb,
+                                               float f1, int half, Fn &&fn) {
+  constexpr int kNT = kMerge ? kOTiles / 2 : kOTiles;
+  const int lane = lane_id_here();
+  f32x4 xn[2] = {};
+  auto xload = [&](int i) {
+    xn[0] = *(const LDS_AS f32x4 *)(xb + ((2 * i) * 64 + lane) * 16);
+    xn[1] = *(const LDS_AS f32x4 *)(xb + ((2 * i + 1) * 64 + lane) * 16);
+  };
+  if constexpr (kMerge) xload(0);
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int i = 2 * t + pp;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = o[t][8 * pp + e] * f;
+      if constexpr (kMerge) {
+        const f32x4 x0 = xn[0], x1 = xn[1];
+        if (i + 1 < 2 * kNT) xload(i + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = __builtin_fmaf(x0[e], f1, v[e]);
+          v[4 + e] = __builtin_fmaf(x1[e], f1, v[4 + e]);
+        }
+      }
+      fn(kMerge ? t + kNT * half : t, pp, v);
+    }
+  }
+}
+
+template <bool kMerge = false>
 __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, uint16_t *base, int row_idx,
-                                           int nrows) {
+                                           int nrows, const LDS_AS uint8_t *xb = nullptr, float f1 = 0.f,
+                                           int half = 0) {
   const int lane = lane_id_here();
   const int r = lane & 31, hl = lane >> 5;
   uint16_t *row = base + (long)row_idx * kHeadDimV + 8 * (1 - hl);
   const bool full = nrows == 32;                      // wave-uniform
-#pragma unroll
-  for (int t = 0; t < kOTiles; ++t) {
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      // piece q holds dims 8q + 4*hl .. +3 of tile t
-      const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);   // q = 2pp
-      const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
-      const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);   // q = 2pp + 1
-      const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
-      // After the swap lanes < 32 hold chunk 2pp + 1 (dims 32t + 16pp + 8 ..),
-      // lanes >= 32 chunk 2pp (dims 32t + 16pp ..).
-      const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
-      if (full || r < nrows) *(u32x4 *)(row + 32 * t + 16 * pp) = u32x4{s0[0], s1[0], s0[1], s1[1]};
-    }
-  }
+  for_each_piece<kMerge>(o, f, xb, f1, half, [&](int t, int pp, const float (&v)[8]) {
+    // piece q holds dims 8q + 4*hl .. +3 of tile t
+    const unsigned a0 = pack_bf16(v[0], v[1]);   // q = 2pp
+    const unsigned a1 = pack_bf16(v[2], v[3]);
+    const unsigned b0 = pack_bf16(v[4], v[5]);   // q = 2pp + 1
+    const unsigned b1 = pack_bf16(v[6], v[7]);
+    // After the swap lanes < 32 hold chunk 2pp + 1 (dims 32t + 16pp + 8 ..),
+    // lanes >= 32 chunk 2pp (dims 32t + 16pp ..).
+    const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+    if (full || r < nrows) *(u32x4 *)(row + 32 * t + 16 * pp) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  });
 }
 
 // Writes this wave's 32 x 512 split partial (times f, rounded to bf16) in
@@ -921,19 +1067,17 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[kOTiles], float f, 
 // last split's epilogue took about 4.1 us that way against 2.0 us this way.
 // Rows past the last real row of the block are written too (the workspace
 // holds whole 32-row blocks) and never read.
-__device__ __forceinline__ void store_acc_block(const f32x16 (&o)[kOTiles], float f, uint16_t *blk) {
+template <bool kMerge = false>
+__device__ __forceinline__ void store_acc_block(const f32x16 (&o)[kOTiles], float f, uint16_t *blk,
+                                                const LDS_AS uint8_t *xb = nullptr, float f1 = 0.f, int half = 0) {
   uint16_t *p = blk + lane_id_here() * 8;
-#pragma unroll
-  for (int t = 0; t < kOTiles; ++t) {
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const unsigned a0 = pack_bf16(o[t][8 * pp + 0] * f, o[t][8 * pp + 1] * f);
-      const unsigned a1 = pack_bf16(o[t][8 * pp + 2] * f, o[t][8 * pp + 3] * f);
-      const unsigned b0 = pack_bf16(o[t][8 * pp + 4] * f, o[t][8 * pp + 5] * f);
-      const unsigned b1 = pack_bf16(o[t][8 * pp + 6] * f, o[t][8 * pp + 7] * f);
-      *(u32x4 *)(p + (2 * t + pp) * 512) = u32x4{a0, a1, b0, b1};
-    }
-  }
+  for_each_piece<kMerge>(o, f, xb, f1, half, [&](int t, int pp, const float (&v)[8]) {
+    const unsigned a0 = pack_bf16(v[0], v[1]);
+    const unsigned a1 = pack_bf16(v[2], v[3]);
+    const unsigned b0 = pack_bf16(v[4], v[5]);
+    const unsigned b1 = pack_bf16(v[6], v[7]);
+    *(u32x4 *)(p + (2 * t + pp) * 512) = u32x4{a0, a1, b0, b1};
+  });
 }
 
 // Bijection of [0, n): workgroup w runs on XCD w % 8 (the dispatcher's
@@ -968,7 +1112,10 @@ __device__ __forceinline__ float row_v_scale(const DecodeArgs &a, int h) {
 
 // kAnyBlock: the cache's block size is a.page_size (a multiple of 16) rather
 // than the 64 tokens of a page, whose slice arithmetic is then shifts.
-template <bool kFp8, bool kSplit, bool kAnyBlock>
+// kKeySplit (bf16 cache, at most 32 rows per workgroup): waves 0 and 1 hold
+// the same 32 rows and take token tiles 0 and 1 of every page (attend_tile);
+// their states merge at the end of each split.
+template <bool kFp8, bool kSplit, bool kAnyBlock, bool kKeySplit = false>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
@@ -992,8 +1139,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   const int b1 = min(max(md[2], b0), a.batch - 1);
   const int nslots = a.batch + a.num_parts - 1;       // partial slots in the workspace
 
-  const int wrow0 = rt * kRowsPerTile + wave * 32;
-  const bool active = wrow0 < a.rows;                 // wave-uniform
+  const int wrow0 = rt * kRowsPerTile + (kKeySplit ? 0 : wave * 32);
+  const bool active = kKeySplit ? wave < 2 : wrow0 < a.rows;   // wave-uniform
   const int qi_min = (rt * kRowsPerTile) / a.group;   // smallest query token of the tile
   // A device-held bmm1 scale replaces the host value (FlashInfer MLA page:
   // bmm1_scale / bmm2_scale may be device tensors).  It cannot be validated
@@ -1153,7 +1300,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       else dma_page_bf16<kSplit>(src, bufs[0], wave);
       have_first = true;
     }
-    if (!staged) load_q(b0);
+    if (!staged && active) load_q(b0);              // waves without rows need no q
   }
   for (int b = b0; b <= b1; ++b) {
     const int L = seq_len(b);
@@ -1189,6 +1336,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     // the same probabilities as rounded for the matrix core (the output's
     // normaliser); equal to l otherwise.
     float m = kNegInf, l = 0.f, lq = 0.f, m_restart = kNegInf;
+    // kKeySplit: wave 0's factors on its own O and on wave 1's (in LDS at merge_buf).
+    float merge_a0 = 1.f, merge_a1 = 0.f;
+    const LDS_AS uint8_t *merge_buf = smem;
+    bool merged = false;                                  // workgroup-uniform
     // O^T accumulators start as the result of an all-zero MFMA so that they
     // live in accumulation registers from the first page on.
     f32x16 o[kOTiles];
@@ -1248,6 +1399,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
             if constexpr (kFp8)
               need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
                                              scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
+            else if constexpr (kKeySplit)
+              need |= attend_tile<kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage + 32 * wave, nvis, scale_log2,
+                                  (j + 1) * kPage > nvis_min, desc_tab, descale, nx, wave);
             else
               need |= attend_page<false, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
                                                  (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
@@ -1263,6 +1417,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         __syncthreads();
         if (!again) {
           have_first = next_has_pages;              // page 0 of b + 1 is in flight into bufs[cur]
+          if constexpr (kKeySplit) {
+            // Waves 0 and 1 hold the states of tiles 0 and 1 of the same
+            // rows; wave w finishes output tiles 8w .. 8w+7 of their merge.
+            // Each sends the other half of its O^T, with its (m, l), through
+            // the buffer of the split's last page (every wave is past it; the
+            // next split's first page goes to the other buffer).  The common
+            // reference is the larger m; each side is scaled by 2^(m - M).
+            LDS_AS uint8_t *xb = bufs[cur ^ 1];
+            if (wave < 2) {
+              // o[8..15] of either wave holds the output tiles its partner
+              // finishes (wave 1 keeps output tiles 8..15 in o[0..7]; see
+              // attend_tile): wave w sends them to region 1 - w.
+              LDS_AS uint8_t *dst = xb + (1 - wave) * 32768;
+#pragma unroll
+              for (int t = 0; t < kOTiles / 2; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                  *(LDS_AS f32x4 *)(dst + ((t * 4 + q4) * 64 + lane) * 16) =
+                      f32x4{o[t + 8][4 * q4], o[t + 8][4 * q4 + 1], o[t + 8][4 * q4 + 2], o[t + 8][4 * q4 + 3]};
+              *(LDS_AS f32x2 *)(xb + 65536 + wave * 512 + lane * 8) = f32x2{m, l};
+            }
+            __syncthreads();
+            if (wave < 2) {
+              const f32x2 ml = *(const LDS_AS f32x2 *)(xb + 65536 + (1 - wave) * 512 + lane * 8);
+              const float M = fmaxf(m, ml[0]);
+              merge_a0 = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - M);
+              merge_a1 = ml[0] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M);
+              // Both waves form the same merged l (the same two terms in
+              // wave order), so their normalisers agree bit for bit.
+              const float l0 = wave == 0 ? l : ml[1], l1 = wave == 0 ? ml[1] : l;
+              const float a_0 = wave == 0 ? merge_a0 : merge_a1, a_1 = wave == 0 ? merge_a1 : merge_a0;
+              l = l0 * a_0 + l1 * a_1;
+              m = M;
+              merge_buf = xb + wave * 32768;
+            }
+            merged = true;
+          }
           break;
         }
         wait_vmcnt<0>();                            // drop the copy of the next split's first page
@@ -1275,8 +1466,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       }
     }
     // The next split's q is loaded first, so its latency hides behind the
-    // epilogue (the next page's wait covers it).
-    if (b < b1) load_q(b + 1);
+    // epilogue (the next page's wait covers it).  With two waves per page the
+    // merging epilogue needs the registers: q follows it.
+    if (!kKeySplit && b < b1 && active) load_q(b + 1);
 
     // Epilogue.  A sequence with one split writes out / lse; otherwise the
     // split writes its normalised output (bf16) and lse to its partial slot,
@@ -1307,17 +1499,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       const int prow = (slot * a.hk + hk) * a.rows + c.rowc;
       const int orow = ((b * a.s_q + c.qi) * a.hq + c.h);
       const int rows_pad = (a.rows + kPartRows - 1) / kPartRows * kPartRows;
-      if (direct && a.pv_descale)
-        store_rows(o, inv * vfac_tab[lane & 31], a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
-      else if (direct)
-        store_rows(o, inv * (a.bmm2_dev ? *a.bmm2_dev : a.v_scale), a.out, orow, max(0, min(32, uniform_here(a.rows) - wrow0)));
-      else
-        store_acc_block(o, inv, a.part_o + ((long)(slot * a.hk + hk) * rows_pad + wrow0) * kHeadDimV);
-      if (lane_id_here() < 32 && c.row < a.rows) {
+      const int nrows = max(0, min(32, uniform_here(a.rows) - wrow0));
+      uint16_t *pblk = a.part_o + ((long)(slot * a.hk + hk) * rows_pad + wrow0) * kHeadDimV;
+      if (kKeySplit && merged) {
+        // Wave w stores output tiles 8w .. 8w+7 of the merged state (its o[0..7]).
+        const float f = direct ? inv * vfac_tab[lane & 31] : inv;
+        if (direct) store_rows<true>(o, f * merge_a0, a.out, orow, nrows, merge_buf, f * merge_a1, wave);
+        else store_acc_block<true>(o, f * merge_a0, pblk, merge_buf, f * merge_a1, wave);
+      } else if (kKeySplit && wave == 1) {
+        // (no pages in this split: wave 0 alone writes the empty result)
+      } else if (direct && (kKeySplit || a.pv_descale)) {
+        store_rows(o, inv * vfac_tab[lane & 31], a.out, orow, nrows);
+      } else if (direct) {
+        store_rows(o, inv * (a.bmm2_dev ? *a.bmm2_dev : a.v_scale), a.out, orow, nrows);
+      } else {
+        store_acc_block(o, inv, pblk);
+      }
+      if (lane_id_here() < 32 && c.row < a.rows && (!kKeySplit || wave == 0)) {
         if (direct) a.lse[((long)b * a.hq + c.h) * a.s_q + c.qi] = lse_v;
         else a.part_lse[prow] = lse_v;
       }
     }
+    if (kKeySplit && b < b1 && active) load_q(b + 1);
   }
 }
 
@@ -1534,8 +1737,15 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), smem, stream, a);
     return hipGetLastError();
   };
+  // At most 32 rows per workgroup (bf16 cache): two waves split each page's tokens.
+  const bool key_split = !a.kv_fp8 && a.rows <= 32;
   auto by_block = [&](auto fp8, auto split) -> hipError_t {
     constexpr bool f = decltype(fp8)::value, s = decltype(split)::value;
+    if constexpr (!f) {
+      if (key_split)
+        return a.page_size == kPage ? launch(mla_decode_kernel<false, s, false, true>)
+                                    : launch(mla_decode_kernel<false, s, true, true>);
+    }
     return a.page_size == kPage ? launch(mla_decode_kernel<f, s, false>) : launch(mla_decode_kernel<f, s, true>);
   };
   using T = std::true_type;

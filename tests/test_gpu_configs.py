@@ -114,10 +114,12 @@ def test_identical_keys_closed_form(gpu_lib):
     assert np.abs(lse[0, :, 0].cpu().numpy() - ref_lse).max() <= 2e-3
 
 
-def test_late_scores_far_above_the_first_keys(gpu_lib):
+@pytest.mark.parametrize("H", [16, 64])
+def test_late_scores_far_above_the_first_keys(gpu_lib, H):
     """A later key scores ~86 (base-2 units) above the first ones: exercises
-    the re-run with a raised reference max."""
-    w = make_workload(seqlens=[300, 150], num_heads_q=16, seed=21)
+    the re-run with a raised reference max (16 heads: two waves per page,
+    one token tile each; 64 heads: one wave per 32 rows)."""
+    w = make_workload(seqlens=[300, 150], num_heads_q=H, seed=21)
     w.q_bits[:] = 0
     w.q_bits[..., 0] = bf16_bits_from_f32(np.array([24.0 * 60.0], dtype=np.float32))[0]
     kv = np.zeros_like(w.kv)

@@ -127,3 +127,17 @@ def test_lds_dma_read_calibration_runs(gpu_lib):
     torch.cuda.synchronize()
     with pytest.raises(mla.MlaError):
         mla.lds_dma_read(torch.ones(1000, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("H,s_q,causal", [(1, 1, False), (16, 1, False), (20, 1, False), (32, 1, False),
+                                          (16, 2, True), (8, 3, True)])
+@pytest.mark.parametrize("parts", [1, 64])
+def test_two_waves_per_page_for_few_rows(gpu_lib, H, s_q, causal, parts):
+    """At most 32 rows per workgroup: two waves take the two token tiles of
+    every page and merge their states at the end of each split.  Lengths put
+    the last visible key in either tile, leave tile 1 empty (L <= 32) and
+    cut splits mid-sequence (64 parts)."""
+    w = make_workload(seqlens=[1, 31, 32, 33, 63, 64, 65, 700, 0, 4000, 97], s_q=s_q, num_heads_q=H,
+                      causal=causal, seed=107 + H)
+    out, lse, _, _ = run_gpu(w, num_parts=parts)
+    compare(w, out, lse, run_oracle(w), label=f"few rows H={H} s_q={s_q} parts={parts}")
