@@ -10,6 +10,7 @@ flash_mla_with_kvcache); they are exported under the C names
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -19,6 +20,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+# Race-check build: page copies never overlap LDS reads (see csrc/mla_decode.hip).
+SERIAL_LIB_PATH = os.path.join(_PKG, "libmla_decode_serial.so")
 
 TILE_MD_INTS = 8
 HEAD_DIM = 576
@@ -39,7 +42,24 @@ def load_library(path: Optional[str] = None):
     global _lib
     if _lib is not None:
         return _lib
-    p = path or LIB_PATH
+    _lib = _open(path or LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def library_variant(path: str):
+    """Within the block, every call goes to the library at path (e.g. the
+    race-check build SERIAL_LIB_PATH) instead of the default one."""
+    global _lib
+    prev = load_library()
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _open(p: str):
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing; build it with __graft_entry__.build() "
                            "(the HIP library is required, there is no CPU fallback)")
@@ -63,7 +83,6 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_fwd_noalloc.argtypes = _DECODE_ARGTYPES[:20] + _DECODE_ARGTYPES[22:]
     lib.mla_lds_dma_read.restype = _c_int
     lib.mla_lds_dma_read.argtypes = [_vp, _c_size, _vp]
-    _lib = lib
     return lib
 
 

@@ -28,21 +28,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# The race-check variant: every page copy issued only after the workgroup is
+# done with the page before it (MLA_SERIAL_COPIES in csrc/mla_decode.hip);
+# its results must equal the default library's bit for bit.
+SERIAL_LIB = os.path.join(PKG, "libmla_decode_serial.so")
+VARIANTS = {LIB: [], SERIAL_LIB: ["-DMLA_SERIAL_COPIES=1"]}
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source into libmla_decode.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every source into libmla_decode.so and the race-check variant
+    libmla_decode_serial.so (always recompiles; the two compile in parallel)."""
+    procs = []
+    for lib, flags in VARIANTS.items():
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), *HIPCC_FLAGS, *flags, *extra_flags, "-I", os.path.join(ROOT, "include"), "-o", tmp,
+               *[os.path.join(CSRC, s) for s in SOURCES]]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((lib, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    failed = []
+    for lib, tmp, pr in procs:
+        outp, _ = pr.communicate()
+        err = "\n".join(l for l in outp.splitlines() if noise not in l)
+        if pr.returncode != 0:
+            failed.append(f"{os.path.basename(lib)}: hipcc failed ({pr.returncode}):\n{err}")
+            continue
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        os.replace(tmp, lib)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

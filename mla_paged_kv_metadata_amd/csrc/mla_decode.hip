@@ -63,6 +63,16 @@ typedef short v2i16 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kRowChunks = kHeadDim * 2 / 16;        // 72 chunks of 16 B per bf16 row
 constexpr int kPageBytes = kPage * kHeadDim * 2;     // 73728
+
+// Race check build (-DMLA_SERIAL_COPIES=1): every page copy is issued only
+// after a barrier that follows the whole workgroup's work on the previous
+// page, so no copy overlaps any LDS read.  Its results must equal the
+// default build's bit for bit (the arithmetic is the same); a difference
+// would point at a copy racing with the reads of the page before it.
+#ifndef MLA_SERIAL_COPIES
+#define MLA_SERIAL_COPIES 0
+#endif
+constexpr bool kSerialCopies = MLA_SERIAL_COPIES != 0;
 constexpr int kPageLoads = kPage * kRowChunks / kThreads;   // 18 DMA loads per thread per bf16 page
 constexpr int kF8RowChunks = kHeadDim / 16;          // 36 chunks per fp8 row
 constexpr int kF8PageBytes = kPage * kHeadDim;       // 36864
@@ -1394,6 +1404,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           nx.src = j + 1 < hi ? page_src(j + 1) : src_of(next_blk, 16 * wave % bs);
           nx.dst = bufs[cur ^ 1];
           nx.wave = wave;
+          const bool copy_later = kSerialCopies && nx.valid;
+          if constexpr (kSerialCopies) nx.valid = false;
           const LDS_AS uint8_t *pg = bufs[cur];
           if (active) {
             if constexpr (kFp8)
@@ -1408,6 +1420,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           } else if (nx.valid) {                    // a wave without rows still copies its share
             if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
             else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
+          }
+          if constexpr (kSerialCopies) {
+            __syncthreads();                        // every wave is done with this page
+            if (copy_later) {
+              if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
+              else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
+            }
           }
           cur ^= 1;
         }
