@@ -36,8 +36,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work_counts(w):
-    """Algorithmic FLOPs and bytes of one decode over workload w."""
+def work_counts(w, q_elem=2):
+    """Algorithmic FLOPs and bytes of one decode over workload w (q_elem: bytes
+    per q element, 1 for an e4m3 query)."""
     L = w.cache_seqlens.astype(np.int64)
     if w.causal:
         n = sum(max(0, min(int(l), int(l) - w.s_q + 1 + i)) for l in L for i in range(w.s_q))
@@ -47,7 +48,7 @@ def work_counts(w):
     flops = 2 * H * (w.head_dim + w.head_dim_v) * n
     e_kv = 1 if w.kv_dtype == "fp8_e4m3fn" else 2
     kv_bytes = int(L.sum()) * w.num_heads_k * w.head_dim * e_kv
-    io_bytes = w.batch * w.s_q * H * (w.head_dim * 2 + w.head_dim_v * 2 + 4)
+    io_bytes = w.batch * w.s_q * H * (w.head_dim * q_elem + w.head_dim_v * 2 + 4)
     return flops, kv_bytes, kv_bytes + io_bytes
 
 
@@ -279,7 +280,7 @@ def trace_summary(cfg, trace_dir, commands, bench_json=None):
     print(open(md).read())
 
 
-def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0, min_s=10.0):
+def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0, min_s=10.0, q_codes=None):
     """The fp64 oracle on the host cores over as many whole sequences as fit the
     budget, timed; the GPU's outputs of the same sequences (out_np, lse_np, from
     the last timed step) are checked against its results on the way.  When the
@@ -298,8 +299,9 @@ def cpu_baseline(w, scale, vs, sinks, out_np, lse_np, budget_s=20.0, min_s=10.0)
     while True:
         for b in range(w.batch):
             t0 = time.perf_counter()
-            ro, rl = oracle_decode(w.q_bits, w.kv, w.kv_dtype, w.block_table, w.cache_seqlens, w.head_dim_v, scale,
-                                   w.causal, vs, batches=[b], sinks=sinks64)
+            ro, rl = oracle_decode(w.q_bits if q_codes is None else q_codes, w.kv, w.kv_dtype, w.block_table,
+                                   w.cache_seqlens, w.head_dim_v, scale, w.causal, vs, batches=[b], sinks=sinks64,
+                                   q_format="bf16" if q_codes is None else "fp8_e4m3fn")
             t_total += time.perf_counter() - t0
             n = sum(max(0, min(int(L[b]), int(L[b]) - w.s_q + 1 + i)) for i in range(w.s_q)) if w.causal \
                 else int(L[b]) * w.s_q
@@ -350,6 +352,8 @@ def main():
     ap.add_argument("--split-cache", action="store_true",
                     help="latent/rope cache and q as separate tensors (mla_decode_fwd_ext)")
     ap.add_argument("--device-scales", action="store_true", help="bmm1/bmm2 scales held on the device")
+    ap.add_argument("--fp8-query", action="store_true",
+                    help="an e4m3 query with a per-tensor q_scale folded into bmm1 (fp8 cache only)")
     ap.add_argument("--page-block-size", type=int, default=64,
                     help="tokens per cache block (a multiple of 16); the same rows re-laid in blocks of this size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -410,15 +414,23 @@ def main():
     if args.page_block_size != w.page_block_size:
         w = repage(w, args.page_block_size, seed=1)
     fp8 = w.kv_dtype == "fp8_e4m3fn"
+    q_codes, q_scale = None, 1.0
+    if args.fp8_query:
+        if not fp8:
+            raise SystemExit("--fp8-query needs an fp8 cache (--config 5)")
+        from workloads import fp8_query
+        q_codes, q_scale = fp8_query(w, seed=1000 + args.config)
     if fp8:
-        s1, s2 = mla.fp8_fused_scales(k_scale=w.k_scale, v_scale=w.v_scale, head_dim_qk=w.head_dim)
+        s1, s2 = mla.fp8_fused_scales(q_scale=q_scale, k_scale=w.k_scale, v_scale=w.v_scale, head_dim_qk=w.head_dim)
     else:
         s1, s2 = w.head_dim ** -0.5, 1.0
-    flops, kv_bytes, alg_bytes = work_counts(w)
+    flops, kv_bytes, alg_bytes = work_counts(w, 1 if args.fp8_query else 2)
     log(f"workload: B={w.batch} H={w.num_heads_q} keys={int(w.cache_seqlens.sum())} pages={w.num_blocks} "
         f"kv={kv_bytes / 1e6:.1f} MB alg={alg_bytes / 1e6:.1f} MB flops={flops / 1e9:.2f} G")
 
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if q_codes is not None:
+        q = torch.from_numpy(np.ascontiguousarray(q_codes)).view(torch.float8_e4m3fn).to(dev)
     if fp8:
         kv_host = torch.from_numpy(w.kv).view(torch.float8_e4m3fn)
     else:
@@ -640,7 +652,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(alg_bytes / fwd_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(t_hbm / fwd_s, 4)}
-    plain = not (args.sinks or args.split_cache or args.device_scales) and w.page_block_size == 64
+    plain = not (args.sinks or args.split_cache or args.device_scales or args.fp8_query) and w.page_block_size == 64
     roof.update({
         "traffic": measured_traffic(args.config) if plain else None,
         "timed": "mla_decode_fwd (split attention + combine), HIP events per call, cold caches",
@@ -659,7 +671,8 @@ def main():
         "copy_kind": "1 GiB device-to-device copy, read + write bytes, best of 5",
     })
     desc = WORKLOAD_NAMES[args.config] + f", H_k={w.num_heads_k} D=576 Dv=512 page={w.page_block_size} seed {args.config}"
-    desc += ", bf16 q ~0.5*N(0,1)" if args.config == 3 else ", bf16 q ~N(0,1)"
+    if not args.fp8_query:
+        desc += ", bf16 q ~0.5*N(0,1)" if args.config == 3 else ", bf16 q ~N(0,1)"
     if fp8:
         desc += f", e4m3fn cache (per-tensor scale {w.k_scale:.4g}), fused bmm1={s1:.4g} bmm2={s2:.4g}"
     else:
@@ -670,6 +683,8 @@ def main():
         desc += ", split latent/rope cache and q"
     if args.device_scales:
         desc += ", device-held bmm1/bmm2 scales"
+    if args.fp8_query:
+        desc += f", e4m3 q (per-tensor q_scale {q_scale:.4g} folded into bmm1)"
     rec = {
         "metric": METRIC,
         "value": round(step_tflops, 2),
@@ -689,7 +704,8 @@ def main():
                    **({"fixed_cost": args.fixed_cost} if args.fixed_cost else {}),
                    "kv_copies": len(kvs),
                    "inputs": "+".join(n for n, f in (("sinks", args.sinks), ("split_cache_q", args.split_cache),
-                                                     ("device_scales", args.device_scales)) if f) or "plain"},
+                                                     ("device_scales", args.device_scales),
+                                                     ("fp8_query", args.fp8_query)) if f) or "plain"},
         "timing": timing,
         "kv_gbps_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_gbps_fwd": round(kv_bytes / fwd_s / 1e9, 1),
@@ -698,7 +714,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"], rec["check"] = cpu_baseline(w, s1, s2, sinks_np, out_np, lse_np)
+        rec["cpu_baseline"], rec["check"] = cpu_baseline(w, s1, s2, sinks_np, out_np, lse_np, q_codes=q_codes)
     print(json.dumps(rec), flush=True)
 
 

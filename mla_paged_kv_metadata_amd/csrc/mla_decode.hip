@@ -798,7 +798,8 @@ template <bool kSplit>
 __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i32x8 (&q8)[18], int s_hi, int s_lo,
                                                f32x16 (&o)[kOTiles], float &m, float &l, float &lq, float &m_restart,
                                                int lane, int key0, int nvis, float scale_log2, bool mask,
-                                               const LDS_AS float *desc, bool descale, const NextPage &nx) {
+                                               const LDS_AS float *desc, bool descale, bool q_lo,
+                                               const NextPage &nx) {
   const int hl = lane >> 5;
   const int r = lane & 31;
   const int k127 = 127;                            // scale 1 for the cache codes
@@ -894,7 +895,8 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
   constexpr int kSoftPieces = 17;
 
   // S^T = K Q^T: step g = 9 tile + kb runs the hi and lo MFMAs of k-block kb
-  // (one accumulation chain per tile); K fragments two steps ahead; one copy
+  // (one accumulation chain per tile; q_lo false, for an e4m3 query whose lo
+  // term is zero, skips the lo MFMAs); K fragments two steps ahead; one copy
   // instruction of the next page every second step (9 per fp8 page).
   constexpr int kPre = 2;
   i32x8 kf[kPre];
@@ -906,7 +908,7 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
     const int g = tile * 9 + kb, sl = g % kPre;
     if (kb == 0) mfma8_first(sc, kf[sl], q8[0], k127, s_hi);
     else mfma8(sc, kf[sl], q8[2 * kb], k127, s_hi);
-    mfma8(sc, kf[sl], q8[2 * kb + 1], k127, s_lo);
+    if (q_lo) mfma8(sc, kf[sl], q8[2 * kb + 1], k127, s_lo);
     if (g + kPre < 18) kf[sl] = kload((g + kPre) % 9, (g + kPre) / 9);
     if (nx.valid && g < 9) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g);
   };
@@ -1410,7 +1412,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           if (active) {
             if constexpr (kFp8)
               need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
-                                             scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
+                                             scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, !a.q_fp8,
+                                             nx);
             else if constexpr (kKeySplit)
               need |= attend_tile<kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage + 32 * wave, nvis, scale_log2,
                                   (j + 1) * kPage > nvis_min, desc_tab, descale, nx, wave);
