@@ -1276,18 +1276,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
     const int base0 = first0 * kPage / bs;
     const int32_t *bt0 = a.block_table + (long)b0 * a.max_blocks;
     bt_pref = bt0[min(base0 + lane, a.max_blocks - 1)];
-    const int len0 = seq_len(b0);
-    const int nblk0 = (len0 + kPage - 1) / kPage;
-    const int hi0 = seq_end(b0, nblk0);
     // (a): the tile's 4 x 32 rows are whole 32-row runs of consecutive q rows
-    // (no split q), and their 4 x 36 KiB fill both page buffers exactly.
+    // (no split q), and their 4 x 36 KiB fill both page buffers exactly.  The
+    // copy depends on the table row alone, so it goes out before the length
+    // of b0 has arrived.
     const bool staged = a.q_rope == nullptr && !a.q_fp8 && a.group % 32 == 0 &&
-                        (rt + 1) * kRowsPerTile <= a.rows && a.q_stride == kHeadDim && hi0 > first0;   // workgroup-uniform
+                        (rt + 1) * kRowsPerTile <= a.rows && a.q_stride == kHeadDim;   // workgroup-uniform
+    LDS_AS uint8_t *region = smem + wave * 32 * kHeadDim * 2;
     if (staged) {
       const int qi = wrow0 / a.group, h0 = hk * a.group + wrow0 % a.group;
       const uint8_t *qblock = (const uint8_t *)(a.q + (((long)b0 * a.s_q + qi) * a.hq + h0) * kHeadDim);
-      LDS_AS uint8_t *region = smem + wave * 32 * kHeadDim * 2;
       stage_q_rows(qblock, region, lane);
+    }
+    const int len0 = seq_len(b0);
+    const int nblk0 = (len0 + kPage - 1) / kPage;
+    const int hi0 = seq_end(b0, nblk0);
+    if (staged) {
       wait_vmcnt<0>();
       if constexpr (kFp8) {
 #pragma unroll
