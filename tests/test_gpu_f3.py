@@ -178,3 +178,43 @@ def test_invalid_log2_scale_gives_nan(gpu_lib, bad):
     out, lse = mla.mla_decode_fwd(q, kv, bt, sl, DV, md, ns, bmm1_scale_log2_tensor=b)
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
+
+
+def test_fp8_query_with_split_cache_is_bitwise_the_joined_cache(gpu_lib):
+    w = make_workload(seqlens=[1, 64, 65, 777, 0, 300], num_heads_q=64, kv_dtype="fp8_e4m3fn", seed=109)
+    _, _, qt = _fp8_q(w, 110)
+    _, kv, bt, sl = to_gpu(w)
+    s1, s2 = scales(w)
+    md, ns = _meta(w, sl, 8)
+    o1, l1 = mla.mla_decode_fwd(qt, kv, bt, sl, DV, md, ns, softmax_scale=s1, v_scale=s2)
+    o2, l2 = mla.mla_decode_fwd(qt, kv[..., :DV].contiguous(), bt, sl, DV, md, ns, softmax_scale=s1, v_scale=s2,
+                                kv_rope=kv[..., DV:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("parts", [1, 16])
+@pytest.mark.parametrize("s_q,causal", [(1, False), (2, True)])
+def test_all_optional_scales_with_two_waves_per_page(gpu_lib, parts, s_q, causal):
+    """16 heads (at most 32 rows: two waves per page, merged per split) with
+    per-head descales, sinks and device-held bmm1 / bmm2 against the oracle."""
+    H = 16
+    w = make_workload(seqlens=[700, 1, 33, 2500, 0, 90], s_q=s_q, num_heads_q=H, causal=causal, seed=113)
+    q, kv, bt, sl = to_gpu(w)
+    s1, s2 = scales(w)
+    s1, s2 = float(np.float32(s1 * 1.2)), float(np.float32(0.8))
+    rng = np.random.default_rng(114)
+    qk = rng.uniform(0.5, 2.0, H).astype(np.float32)
+    pv = rng.uniform(0.5, 2.0, H).astype(np.float32)
+    sinks = np.linspace(-1.0, 3.0, H).astype(np.float32)
+    md, ns = _meta(w, sl, parts)
+    out, lse = mla.mla_decode_fwd(q, kv, bt, sl, DV, md, ns, softmax_scale=5.0, v_scale=7.0, causal=causal,
+                                  bmm1_scale_tensor=torch.tensor([s1], dtype=torch.float32, device="cuda"),
+                                  bmm2_scale_tensor=torch.tensor([s2], dtype=torch.float32, device="cuda"),
+                                  qk_descale=torch.from_numpy(qk).cuda(), pv_descale=torch.from_numpy(pv).cuda(),
+                                  sinks=torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    ref = oracle_decode(w.q_bits, w.kv, w.kv_dtype, w.block_table, w.cache_seqlens, DV, s1, causal, s2,
+                        sinks=sinks.astype(np.float64), qk_descale=qk.astype(np.float64),
+                        pv_descale=pv.astype(np.float64))
+    compare(w, out, lse, ref, label=f"two waves per page, all scales, s_q={s_q} parts={parts}")
