@@ -58,6 +58,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -743,13 +744,17 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w 
 // In place: q8[2kb] / q8[2kb+1] hold the bf16 q values of k-block kb's bytes
 // 0..15 / 16..31 (16 bf16 each, loaded by q_chunk_f8); they become the hi and
 // lo e4m3 terms (32 codes each).  s_hi / s_lo: the B-operand E8M0 scales.
+// The lo conversion takes its factor 16 through the instruction's scale
+// operand (a conversion to e4m3 divides by it): lo = e4m3((v - hv) / 2^-4).
 __device__ __forceinline__ void quantize_q_f8(i32x8 (&q8)[18], int &s_hi, int &s_lo) {
-  float mx = 0.f;
+  // Largest |q|: bf16 magnitudes (sign bits cleared) order as 16-bit integers.
+  u16x2 mxv = {0, 0};
 #pragma unroll
   for (int i = 0; i < 18; ++i)
 #pragma unroll
     for (int w = 0; w < 8; ++w)
-      mx = fmaxf(mx, fmaxf(fabsf(bf16_lo((unsigned)q8[i][w])), fabsf(bf16_hi((unsigned)q8[i][w]))));
+      mxv = __builtin_elementwise_max(mxv, __builtin_bit_cast(u16x2, (unsigned)q8[i][w] & 0x7fff7fffu));
+  float mx = __uint_as_float((unsigned)max(mxv[0], mxv[1]) << 16);
   mx = max_across_halves(mx);                     // the head's largest |q| (both lane halves)
   // mx = f 2^x, f in [1, 2): e = 7 - x puts 2^e mx in [128, 256).
   const int x = ((__float_as_int(mx) >> 23) & 255) - 127;
@@ -773,8 +778,10 @@ __device__ __forceinline__ void quantize_q_f8(i32x8 (&q8)[18], int &s_hi, int &s
       const unsigned h = pack_e4m3(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3]);
       const f32x4 hv = unpack_e4m3(h);
       hi[d] = (int)h;
-      lo[d] = (int)pack_e4m3(16.f * (v[4 * d] - hv[0]), 16.f * (v[4 * d + 1] - hv[1]), 16.f * (v[4 * d + 2] - hv[2]),
-                             16.f * (v[4 * d + 3] - hv[3]));
+      v2i16 r = {0, 0};
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v[4 * d] - hv[0], v[4 * d + 1] - hv[1], 0.0625f, false);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v[4 * d + 2] - hv[2], v[4 * d + 3] - hv[3], 0.0625f, true);
+      lo[d] = (int)__builtin_bit_cast(unsigned, r);
     }
     q8[2 * kb] = hi;
     q8[2 * kb + 1] = lo;
