@@ -788,6 +788,19 @@ __device__ __forceinline__ void quantize_q_f8(i32x8 (&q8)[18], int &s_hi, int &s
   }
 }
 
+// Holds a value at this point of the instruction stream: an empty volatile
+// asm that reads and rewrites it keeps its place among the matrix-core steps
+// (inline asm), so the work producing the value cannot sink past them to
+// where the value is used.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_elem(f32x16 &v, int i) {
+  float x = v[i];
+  pin(x);
+  v[i] = x;
+}
+
 // Score steps on the fp8 matrix core with the accumulator in ordinary VGPRs
 // (see mfma_qk_first); sa / sb: the E8M0 scales of the A and B operands.
 __device__ __forceinline__ void mfma8_first(f32x16 &s, const i32x8 &a, const i32x8 &b, int sa, int sb) {
@@ -799,14 +812,49 @@ __device__ __forceinline__ void mfma8(f32x16 &s, const i32x8 &a, const i32x8 &b,
       : "+v"(s) : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
 
+// V^T of dim tile mt for one PV step over 64 tokens taken from two pages:
+// tokens 32..63 of page `a` (k 0..31) and tokens 0..31 of page `b` (k
+// 32..63), by four 8-bit transposing reads (R = 0..3: bytes 8R .. 8R+7 =
+// tokens 16R + 8 (e / 4) + 4h + (e % 4) of the 64 k positions, e = 0..7).
+// In each 16-lane group G output lane i gets byte i % 8 of the rows loaded
+// by lanes 2e + i / 8, so source lane (G, s) loads token 16R + 8 (s / 8) +
+// 4 (G / 2) + (s / 2) % 4, dims 32 mt + 16 (G % 2) + 8 (s % 2): chunk
+// 2 (mt % 2) + G % 2 of group mt / 2, swizzled by ((t >> 2) & 3) =
+// (2 (s / 8) + G / 2) & 3 (the same for t and t + 32).
+struct VtPair {
+  int off0, off1;                                  // lane offsets for even / odd dim tiles
+  __device__ __forceinline__ explicit VtPair(int lane) {
+    const int G = lane >> 4, sl16 = lane & 15;
+    const int fv = (2 * (sl16 >> 3) + (G >> 1)) & 3;
+    const int vlane = 64 * (8 * (sl16 >> 3) + 4 * (G >> 1) + ((sl16 >> 1) & 3)) + 8 * (sl16 & 1);
+    off0 = vlane + 16 * ((G & 1) ^ fv);
+    off1 = vlane + 16 * ((2 + (G & 1)) ^ fv);
+  }
+  __device__ __forceinline__ i32x8 load(const LDS_AS uint8_t *a, const LDS_AS uint8_t *b, int mt) const {
+    const int o = ((mt & 1) ? off1 : off0) + 4096 * (mt >> 1);
+    const v2i32 x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(a + o + 2048));
+    const v2i32 x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(a + o + 3072));
+    const v2i32 x2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(b + o));
+    const v2i32 x3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(b + o + 1024));
+    return i32x8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+  }
+};
+
 // One 64-token fp8 page for this wave's 32 rows on the fp8 matrix core (the
 // fp8 counterpart of attend_page; same reference-max scheme and return).
+// The PV step of a page pairs the previous page's tile 1 (k 0..31: its
+// weights p1 with block exponent e1, carried in and out) with this page's
+// tile 0 (k 32..63), so that this page's tile-1 softmax runs under the PV
+// MFMAs instead of before them; at a split's first page (has_prev false) the
+// first half has zero weights (over finite rows of this page), and
+// attend_drain_f8 adds the last page's tile 1 after the split.
 template <bool kSplit>
 __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i32x8 (&q8)[18], int s_hi, int s_lo,
                                                f32x16 (&o)[kOTiles], float &m, float &l, float &lq, float &m_restart,
                                                int lane, int key0, int nvis, float scale_log2, bool mask,
                                                const LDS_AS float *desc, bool descale, bool q_lo,
-                                               const NextPage &nx) {
+                                               const NextPage &nx, const LDS_AS uint8_t *prev_pg,
+                                               bool has_prev, u32x4 &p1, int &e1) {
   const int hl = lane >> 5;
   const int r = lane & 31;
   const int k127 = 127;                            // scale 1 for the cache codes
@@ -822,25 +870,9 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
     const u32x4 y = *(const LDS_AS u32x4 *)(kc + 4096 * kb + 2048 * tile);
     return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
   };
-  // V^T of dim tile mt by four 8-bit transposing reads (R = 0..3: bytes
-  // 8R .. 8R+7 = tokens 16R + 8 (e / 4) + 4h + (e % 4), e = 0..7).  In each
-  // 16-lane group G output lane i gets byte i % 8 of the rows loaded by lanes
-  // 2e + i / 8, so source lane (G, s) loads token 16R + 8 (s / 8) + 4 (G / 2)
-  // + (s / 2) % 4, dims 32 mt + 16 (G % 2) + 8 (s % 2): chunk 2 (mt % 2) +
-  // G % 2 of group mt / 2, swizzled by ((t >> 2) & 3) = (2 (s / 8) + G / 2) & 3.
-  const int G = lane >> 4, sl16 = lane & 15;
-  const int fv = (2 * (sl16 >> 3) + (G >> 1)) & 3;
-  const int vlane = 64 * (8 * (sl16 >> 3) + 4 * (G >> 1) + ((sl16 >> 1) & 3)) + 8 * (sl16 & 1);
-  const LDS_AS uint8_t *vb0 = pg + vlane + 16 * ((G & 1) ^ fv);
-  const LDS_AS uint8_t *vb1 = pg + vlane + 16 * ((2 + (G & 1)) ^ fv);
-  auto vload = [&](int mt) -> i32x8 {
-    const LDS_AS uint8_t *p = ((mt & 1) ? vb1 : vb0) + 4096 * (mt >> 1);
-    const v2i32 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)p);
-    const v2i32 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 1024));
-    const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 2048));
-    const v2i32 d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i32 *)(p + 3072));
-    return i32x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  };
+  const VtPair vt(lane);
+  const LDS_AS uint8_t *va = has_prev ? prev_pg : pg;
+  auto vload = [&](int mt) -> i32x8 { return vt.load(va, pg, mt); };
 
   // Online softmax of one 32-token tile in 17 pieces (as in attend_page): in
   // S^T a lane holds head r and tokens (i/4)*8 + 4*hl + i%4 of the tile.
@@ -864,10 +896,13 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
           if (tok >= nvis) sc[i] = kNegInf;
         }
       }
+#pragma unroll
+      for (int i = 8 * piece; i < 8 * piece + 8; ++i) pin_elem(sc, i);
     } else if (piece < 6) {
       const int i0 = 4 * (piece - 2);
       const float t = fmaxf(fmaxf(sc[i0], sc[i0 + 1]), fmaxf(sc[i0 + 2], sc[i0 + 3]));
       mx = piece == 2 ? t : fmaxf(mx, t);
+      pin(mx);
     } else if (piece == 6) {
       float t = max_across_halves(mx);
       t = (t == kNegInf) ? kNegInf : t * scale_log2;
@@ -879,11 +914,16 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
       const int e = t == kNegInf ? 0 : (int)floorf(t - mu);
       et[tile] = max(-100, min(100, e));
       mu += (float)et[tile];
+      pin(mu);
+      pin(et[tile]);
     } else if (piece < 15) {
       const int i0 = 2 * (piece - 7);
       sc[i0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0], scale_log2, -mu));
       sc[i0 + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0 + 1], scale_log2, -mu));
       ps = (piece == 7 ? 0.f : ps) + (sc[i0] + sc[i0 + 1]);
+      pin_elem(sc, i0);
+      pin_elem(sc, i0 + 1);
+      pin(ps);
     } else if (piece == 15) {
       psq = 0.f;
 #pragma unroll
@@ -892,11 +932,15 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
         p8[tile][d] = c;
         const f32x4 back = unpack_e4m3(c);
         psq += (back[0] + back[1]) + (back[2] + back[3]);
+        asm volatile("" : "+v"(p8[tile]));
       }
+      pin(psq);
     } else {
       const float w = pow2f(et[tile]);
       l += sum_across_halves(ps) * w;
       lq += sum_across_halves(psq) * w;
+      pin(l);
+      pin(lq);
     }
   };
   constexpr int kSoftPieces = 17;
@@ -911,42 +955,55 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
   for (int i = 0; i < kPre; ++i) kf[i] = kload(i, 0);
   __builtin_amdgcn_sched_barrier(0);
   f32x16 s0, s1;
-  auto qk_step = [&](f32x16 &sc, int tile, int kb) {
+  // A step's VALU work sits between its MFMAs: the two MFMAs of a step (and
+  // the next step's) form one accumulation chain, so the wave cannot issue
+  // past an MFMA until its predecessor is done, and only instructions placed
+  // right after an MFMA run under it.  `mid` runs after the hi MFMA, `post`
+  // (with the K reads and the copy) after the lo one.
+  auto qk_step = [&](f32x16 &sc, int tile, int kb, auto &&mid, auto &&post) {
     const int g = tile * 9 + kb, sl = g % kPre;
     if (kb == 0) mfma8_first(sc, kf[sl], q8[0], k127, s_hi);
     else mfma8(sc, kf[sl], q8[2 * kb], k127, s_hi);
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
     if (q_lo) mfma8(sc, kf[sl], q8[2 * kb + 1], k127, s_lo);
+    __builtin_amdgcn_sched_barrier(0);
     if (g + kPre < 18) kf[sl] = kload((g + kPre) % 9, (g + kPre) / 9);
     if (nx.valid && g < 9) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g);
+    post();
   };
+  auto nothing = [] {};
 #pragma unroll
   for (int kb = 0; kb < 9; ++kb) {
-    qk_step(s0, 0, kb);
+    qk_step(s0, 0, kb, nothing, nothing);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Tile 1, with tile 0's softmax: two pieces after each of its steps.
+  // Tile 1, with tile 0's softmax: one piece after each of its MFMAs.
 #pragma unroll
   for (int kb = 0; kb < 9; ++kb) {
-    qk_step(s1, 1, kb);
-    if (kb == 0) mfma_qk_drain(s0);
-#pragma unroll
-    for (int pc = 2 * kb; pc < 2 * kb + 2; ++pc)
-      if (pc < kSoftPieces) soft(s0, 0, key0, pc);
+    qk_step(
+        s1, 1, kb,
+        [&] {
+          if (kb == 0) mfma_qk_drain(s0);
+          soft(s0, 0, key0, 2 * kb);
+        },
+        [&] {
+          if (2 * kb + 1 < kSoftPieces) soft(s0, 0, key0, 2 * kb + 1);
+        });
     __builtin_amdgcn_sched_barrier(0);
   }
-  // First V^T operands, then tile 1's softmax.
-  constexpr int kVPre = 2;
+  // PV: the previous page's tile 1 and this page's tile 0 (P^T bytes 0..15
+  // and 16..31; lane half 0 supplies the first one's block scale, half 1 the
+  // second's), with this page's tile-1 softmax one piece after each MFMA.
+  constexpr int kVPre = 1;                         // one ahead: two spill in the split-cache and any-block kernels
   i32x8 vf[kVPre];
 #pragma unroll
   for (int i = 0; i < kVPre; ++i) vf[i] = vload(i);
+  const i32x8 pt = {has_prev ? (int)p1[0] : 0, has_prev ? (int)p1[1] : 0, has_prev ? (int)p1[2] : 0,
+                    has_prev ? (int)p1[3] : 0, (int)p8[0][0], (int)p8[0][1], (int)p8[0][2], (int)p8[0][3]};
+  const int ps_scale = 127 + (hl ? et[0] : (has_prev ? e1 : 0));
   mfma_qk_drain(s1);
-#pragma unroll
-  for (int pc = 0; pc < kSoftPieces; ++pc) soft(s1, 1, key0 + 32, pc);
-  // P^T: bytes 0..15 tile 0, bytes 16..31 tile 1; lane half h supplies the
-  // block scale of tile h.
-  const i32x8 pt = {(int)p8[0][0], (int)p8[0][1], (int)p8[0][2], (int)p8[0][3],
-                    (int)p8[1][0], (int)p8[1][1], (int)p8[1][2], (int)p8[1][3]};
-  const int ps_scale = 127 + (hl ? et[1] : et[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mt = 0; mt < kOTiles; ++mt) {
@@ -954,8 +1011,37 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
     o[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[sl], pt, o[mt], 0, 0, 0, k127, 0, ps_scale);
     if (mt + kVPre < kOTiles) vf[sl] = vload(mt + kVPre);
     __builtin_amdgcn_sched_barrier(0);               // keep the V^T loads kVPre steps ahead
+    soft(s1, 1, key0 + 32, mt);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  soft(s1, 1, key0 + 32, kSoftPieces - 1);
+  p1 = p8[1];
+  e1 = et[1];
   return __ballot(need) != 0;
+}
+
+// The PV step left over at the end of a split: the last page's tile 1 (p1,
+// block exponent e1) as the first half, zero weights over that page's
+// tokens 0..31 (finite rows) as the second.
+__device__ __forceinline__ void attend_drain_f8(const LDS_AS uint8_t *pg, const u32x4 &p1, int e1,
+                                                f32x16 (&o)[kOTiles], int lane) {
+  const int hl = lane >> 5;
+  const int k127 = 127;
+  const VtPair vt(lane);
+  const i32x8 pt = {(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3], 0, 0, 0, 0};
+  const int ps_scale = 127 + (hl ? 0 : e1);
+  constexpr int kVPre = 2;
+  i32x8 vf[kVPre];
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) vf[i] = vt.load(pg, pg, i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mt = 0; mt < kOTiles; ++mt) {
+    const int sl = mt % kVPre;
+    o[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[sl], pt, o[mt], 0, 0, 0, k127, 0, ps_scale);
+    if (mt + kVPre < kOTiles) vf[sl] = vt.load(pg, pg, mt + kVPre);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Number of passes a segment may take when a score overshoots the reference
@@ -1139,7 +1225,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   LDS_AS uint8_t *smem = (LDS_AS uint8_t *)smem_raw;
   // Two page buffers: 72 KiB each for bf16, 36 KiB each for fp8.
-  LDS_AS uint8_t *const bufs[2] = {smem, smem + (kFp8 ? kF8PageBytes : kPageBytes)};
+  // Page buffers: two for bf16 pages; three for fp8 pages, whose PV step
+  // still reads the previous page while the next one is copied.
+  constexpr int kBufs = kFp8 ? 3 : 2;
+  LDS_AS uint8_t *const bufs[3] = {smem, smem + (kFp8 ? kF8PageBytes : kPageBytes), smem + 2 * kF8PageBytes};
+  auto buf_next = [](int i) { return i + 1 == kBufs ? 0 : i + 1; };
+  auto buf_prev = [](int i) { return i == 0 ? kBufs - 1 : i - 1; };
   volatile LDS_AS int *rerun_flag = (volatile LDS_AS int *)(smem + 2 * kPageBytes);
 
   const int tid = threadIdx.x;
@@ -1396,6 +1487,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
       }
       for (int pass = 0;; ++pass) {
         bool need = false;
+        // fp8: the previous page's tile-1 weights, not yet in O (see attend_page_f8).
+        bool has_prev = false;
+        u32x4 p1 = {0, 0, 0, 0};
+        int e1 = 0;
         if (!have_first) {
           if (kFp8) dma_page_fp8<kSplit>(page_src(lo), bufs[cur], wave);
           else dma_page_bf16<kSplit>(page_src(lo), bufs[cur], wave);
@@ -1415,7 +1510,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           NextPage nx;
           nx.valid = j + 1 < hi || next_has_pages;
           nx.src = j + 1 < hi ? page_src(j + 1) : src_of(next_blk, 16 * wave % bs);
-          nx.dst = bufs[cur ^ 1];
+          nx.dst = bufs[buf_next(cur)];
           nx.wave = wave;
           const bool copy_later = kSerialCopies && nx.valid;
           if constexpr (kSerialCopies) nx.valid = false;
@@ -1424,7 +1519,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
             if constexpr (kFp8)
               need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
                                              scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, !a.q_fp8,
-                                             nx);
+                                             nx, bufs[buf_prev(cur)], has_prev, p1, e1);
             else if constexpr (kKeySplit)
               need |= attend_tile<kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage + 32 * wave, nvis, scale_log2,
                                   (j + 1) * kPage > nvis_min, desc_tab, descale, nx, wave);
@@ -1442,8 +1537,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
               else dma_page_bf16<kSplit>(nx.src, nx.dst, wave);
             }
           }
-          cur ^= 1;
+          has_prev = true;
+          cur = buf_next(cur);
         }
+        // fp8: the last page's tile 1 (its buffer is intact: the next
+        // split's first page went to the buffer after it).
+        if (kFp8 && active && has_prev) attend_drain_f8(bufs[buf_prev(cur)], p1, e1, o, lane);
         if (need && lane == 0) *rerun_flag = 1;
         __syncthreads();
         const bool again = (*rerun_flag != 0) && (pass + 1 < kMaxPasses);   // workgroup-uniform
@@ -1457,7 +1556,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
             // the buffer of the split's last page (every wave is past it; the
             // next split's first page goes to the other buffer).  The common
             // reference is the larger m; each side is scaled by 2^(m - M).
-            LDS_AS uint8_t *xb = bufs[cur ^ 1];
+            LDS_AS uint8_t *xb = bufs[buf_next(cur)];
             if (wave < 2) {
               // o[8..15] of either wave holds the output tiles its partner
               // finishes (wave 1 keeps output tiles 8..15 in o[0..7]; see
