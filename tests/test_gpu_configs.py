@@ -133,3 +133,31 @@ def test_late_scores_far_above_the_first_keys(gpu_lib, H):
     w.kv = kv
     out, lse, _, _ = run_gpu(w)
     compare(w, out, lse, run_oracle(w), label="late large score")
+
+
+def _e4m3_codes(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("H,parts", [(16, None), (64, None), (64, 1)])
+def test_late_scores_far_above_the_first_keys_fp8(gpu_lib, H, parts):
+    """The re-run with a raised reference max on the fp8 path, whose PV steps
+    carry each page's second token tile into the next step: a key ~86 base-2
+    units above the first ones on a middle page (unit scales)."""
+    w = make_workload(seqlens=[300, 150, 600], num_heads_q=H, kv_dtype="fp8_e4m3fn", seed=22)
+    w.k_scale, w.v_scale = 1.0, 1.0
+    w.q_bits[:] = 0
+    w.q_bits[..., 0] = bf16_bits_from_f32(np.array([24.0 * 60.0], dtype=np.float32))[0]
+    w.q_bits[..., 1] = bf16_bits_from_f32(np.array([0.5], dtype=np.float32))[0]
+    kv = np.zeros_like(w.kv)
+    for b, t_big in [(0, 250), (1, 70), (2, 390)]:
+        L = int(w.cache_seqlens[b])
+        for t in range(L):
+            page, r = w.block_table[b, t // 64], t % 64
+            kv[page, r, 0, 1] = _e4m3_codes([float(t % 7 - 3)])[0]
+            kv[page, r, 0, 2 + t % 500] = _e4m3_codes([float(t % 5 - 2) * 0.5])[0]
+        page, r = w.block_table[b, t_big // 64], t_big % 64
+        kv[page, r, 0, 0] = _e4m3_codes([1.0])[0]
+    w.kv = kv
+    out, lse, _, _ = run_gpu(w, num_parts=parts)
+    compare(w, out, lse, run_oracle(w), label=f"fp8 late large score H={H} parts={parts}")
