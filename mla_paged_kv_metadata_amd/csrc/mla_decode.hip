@@ -847,8 +847,9 @@ struct VtPair {
 // tile 0 (k 32..63), so that this page's tile-1 softmax runs under the PV
 // MFMAs instead of before them; at a split's first page (has_prev false) the
 // first half has zero weights (over finite rows of this page), and
-// attend_drain_f8 adds the last page's tile 1 after the split.
-template <bool kSplit>
+// attend_drain_f8 adds the last page's tile 1 after the split.  kVPre: V^T
+// operands that many MFMAs ahead.
+template <bool kSplit, int kVPre>
 __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i32x8 (&q8)[18], int s_hi, int s_lo,
                                                f32x16 (&o)[kOTiles], float &m, float &l, float &lq, float &m_restart,
                                                int lane, int key0, int nvis, float scale_log2, bool mask,
@@ -996,7 +997,6 @@ __device__ __forceinline__ bool attend_page_f8(const LDS_AS uint8_t *pg, const i
   // PV: the previous page's tile 1 and this page's tile 0 (P^T bytes 0..15
   // and 16..31; lane half 0 supplies the first one's block scale, half 1 the
   // second's), with this page's tile-1 softmax one piece after each MFMA.
-  constexpr int kVPre = 1;                         // one ahead: two spill in the split-cache and any-block kernels
   i32x8 vf[kVPre];
 #pragma unroll
   for (int i = 0; i < kVPre; ++i) vf[i] = vload(i);
@@ -1517,7 +1517,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
           const LDS_AS uint8_t *pg = bufs[cur];
           if (active) {
             if constexpr (kFp8)
-              need |= attend_page_f8<kSplit>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
+              // (V^T two ahead spills in the split-cache and any-block kernels)
+              need |= attend_page_f8<kSplit, kSplit || kAnyBlock ? 1 : 2>(pg, q8, s_hi, s_lo, o, m, l, lq, m_restart, lane, j * kPage, nvis,
                                              scale_log2, (j + 1) * kPage > nvis_min, desc_tab, descale, !a.q_fp8,
                                              nx, bufs[buf_prev(cur)], has_prev, p1, e1);
             else if constexpr (kKeySplit)
