@@ -67,11 +67,17 @@ WORKLOAD_NAMES = {1: "tiny MLA decode: B=2 s_q=1 H_q=16 L={127,300}",
 
 
 def decode_source_hash():
+    """Hash of the kernels' sources with comments and blank space removed, so
+    that an edit of the comments alone keeps a counter summary current."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

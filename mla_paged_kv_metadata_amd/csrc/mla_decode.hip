@@ -15,9 +15,9 @@
 //    table: a contiguous page range) for a 128-row tile of one KV head; each
 //    wave owns 32 rows (query heads, with s_q folded into rows).
 //  * Pages are streamed HBM -> LDS with 16-byte LDS-DMA loads
-//    (global_load_lds_dwordx4), double buffered (2 x 72 KiB).  Chunks are
-//    XOR-swizzled within each 1152-byte row so that MFMA operand reads hit
-//    distinct banks.
+//    (global_load_lds_dwordx4): bf16 pages double buffered (2 x 72 KiB), fp8
+//    pages in three 36 KiB buffers.  Chunks are XOR-swizzled within each row
+//    so that MFMA operand reads hit distinct banks.
 //  * Scores are computed transposed, S^T[token][head] = K Q^T, on
 //    v_mfma_f32_32x32x16_bf16 with K from LDS and Q^T resident in VGPRs.
 //    In that layout each lane holds one head and 32 of the page's 64 tokens,
@@ -33,10 +33,11 @@
 //    sequence writes bf16 partials (O/l) and fp32 lse that the combine
 //    kernel merges.
 //  * fp8 (e4m3fn) caches stay as codes in LDS (half the bytes of a bf16
-//    page); each 8-code operand fragment is converted exactly to bf16 in
-//    registers just before its MFMA (every e4m3fn value is a bf16 value).
-//    The fused bmm1/bmm2 scales of the FlashInfer MLA page enter as
-//    softmax_scale and v_scale.
+//    page) and feed the fp8 matrix core (v_mfma_scale_f32_32x32x64_f8f6f4)
+//    as they are: q enters as two e4m3 terms (hi + lo / 16, one power-of-two
+//    block scale per head) and P as one e4m3 term per 32-token tile with a
+//    block exponent.  The fused bmm1/bmm2 scales of the FlashInfer MLA page
+//    enter as softmax_scale and v_scale.
 #include "mla_kernels.h"
 #include <algorithm>
 #include <mutex>
