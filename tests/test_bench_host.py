@@ -81,6 +81,18 @@ def test_measured_traffic_needs_the_current_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic(2) is None
 
 
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    a = tmp_path / "a.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "DECODE_SOURCES", ["a.hip"])
+    a.write_text("int f() { return 1; }  // one\n/* block\n comment */\n")
+    h0 = bench.decode_source_hash()
+    a.write_text("// other words\nint f()   {\n return 1; }\n")
+    assert bench.decode_source_hash() == h0
+    a.write_text("int f() { return 2; }\n")
+    assert bench.decode_source_hash() != h0
+
+
 def test_more_than_one_gpu_is_refused_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
