@@ -46,11 +46,15 @@ def test_config2_full(gpu_lib):
     compare(w, out, lse, run_oracle(w), label="c2 full")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("parts", [1, 7, 64, 256, 1024])
-def test_split_count_does_not_change_result(gpu_lib, parts):
-    w = make_workload(seqlens=[3000, 65, 1, 1800, 640], num_heads_q=128, seed=31)
+def test_split_count_does_not_change_result(gpu_lib, parts, kv_dtype):
+    """Any split count (down to one page per split, where an fp8 split's PV
+    steps are its first page's and the closing one only) gives the oracle's
+    result."""
+    w = make_workload(seqlens=[3000, 65, 1, 1800, 640], num_heads_q=128, kv_dtype=kv_dtype, seed=31)
     out, lse, md, ns = run_gpu(w, num_parts=parts)
-    compare(w, out, lse, run_oracle(w), label=f"parts={parts}")
+    compare(w, out, lse, run_oracle(w), label=f"parts={parts} {kv_dtype}")
 
 
 @pytest.mark.parametrize("parts,fc", [(1, 1), (7, 2), (256, 9), (300, 3)])
