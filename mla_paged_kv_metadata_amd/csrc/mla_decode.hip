@@ -1499,7 +1499,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
         have_first = false;
         for (int j = lo; j < hi; ++j) {
           // Page j has landed in every wave's share; every wave is done with
-          // the other buffer, which the copy of the next page reuses.
+          // the buffer that the copy of the next page reuses (the previous
+          // page's with two buffers; the one before it with three, where the
+          // previous page is still read by this page's PV step).
           wait_vmcnt<0>();
           __syncthreads();
           const int nvalid = min(kPage, L - j * kPage);
