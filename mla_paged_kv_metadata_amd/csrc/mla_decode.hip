@@ -120,6 +120,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // alike, so M0 is lowered by it.  Cache pages are read exactly once, so the
 // copy carries the non-temporal hint: the lines it brings into L2 go first,
 // and q rows and partial outputs (which are reused) stay resident longer.
+// M0 is listed as clobbered; the compiler warns that it may not preserve a
+// reserved register across the asm, which is harmless here because nothing
+// else in these kernels uses M0 (a CPU test compiles them and checks that
+// every M0 write in the code is one of these).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int kImm, bool kNt = true>
 __device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) {
   static_assert(kImm >= 0 && kImm < 4096, "global offset field");
@@ -133,6 +139,7 @@ __device__ __forceinline__ void lds_dma16(const uint8_t *src, LDS_AS void *lds) 
                  "n"(kImm)
                  : "m0");
 }
+#pragma clang diagnostic pop
 
 // q rows of a wave staged through LDS: the wave's 32 consecutive q rows
 // (32 x 1152 B, contiguous in memory) are copied as 36 LDS-DMA instructions
