@@ -360,6 +360,8 @@ def main():
     ap.add_argument("--device-scales", action="store_true", help="bmm1/bmm2 scales held on the device")
     ap.add_argument("--fp8-query", action="store_true",
                     help="an e4m3 query with a per-tensor q_scale folded into bmm1 (fp8 cache only)")
+    ap.add_argument("--batch-share", type=int, default=1, metavar="N",
+                    help="time one GPU's share of the batch split over N GPUs (its first B/N sequences)")
     ap.add_argument("--page-block-size", type=int, default=64,
                     help="tokens per cache block (a multiple of 16); the same rows re-laid in blocks of this size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -395,7 +397,7 @@ def main():
     import torch
 
     import mla_paged_kv_metadata_amd as mla
-    from workloads import make_config, repage
+    from workloads import batch_share, make_config, repage
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -417,6 +419,8 @@ def main():
     mla.load_library()
     dev = torch.device("cuda:0")
     w = make_config(args.config)
+    if args.batch_share > 1:
+        w = batch_share(w, args.batch_share)
     if args.page_block_size != w.page_block_size:
         w = repage(w, args.page_block_size, seed=1)
     fp8 = w.kv_dtype == "fp8_e4m3fn"
@@ -658,7 +662,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(alg_bytes / fwd_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(t_hbm / fwd_s, 4)}
-    plain = not (args.sinks or args.split_cache or args.device_scales or args.fp8_query) and w.page_block_size == 64
+    plain = (not (args.sinks or args.split_cache or args.device_scales or args.fp8_query) and w.page_block_size == 64
+             and args.batch_share == 1)
     roof.update({
         "traffic": measured_traffic(args.config) if plain else None,
         "timed": "mla_decode_fwd (split attention + combine), HIP events per call, cold caches",
@@ -691,6 +696,9 @@ def main():
         desc += ", device-held bmm1/bmm2 scales"
     if args.fp8_query:
         desc += f", e4m3 q (per-tensor q_scale {q_scale:.4g} folded into bmm1)"
+    if args.batch_share > 1:
+        desc += (f"; one GPU's share of the batch over {args.batch_share} GPUs: its first {w.batch} sequences "
+                 "and their cache blocks")
     rec = {
         "metric": METRIC,
         "value": round(step_tflops, 2),
@@ -709,6 +717,7 @@ def main():
                    "kv_dtype": w.kv_dtype, "total_keys": int(w.cache_seqlens.sum()), "num_parts": P,
                    **({"fixed_cost": args.fixed_cost} if args.fixed_cost else {}),
                    "kv_copies": len(kvs),
+                   **({"batch_share_of_gpus": args.batch_share} if args.batch_share > 1 else {}),
                    "inputs": "+".join(n for n, f in (("sinks", args.sinks), ("split_cache_q", args.split_cache),
                                                      ("device_scales", args.device_scales),
                                                      ("fp8_query", args.fp8_query)) if f) or "plain"},

@@ -9,7 +9,7 @@ import torch
 
 import mla_paged_kv_metadata_amd as mla
 from oracle import bf16_bits_to_f64
-from workloads import bf16_bits_from_f32, make_config, make_workload
+from workloads import batch_share, bf16_bits_from_f32, make_config, make_workload
 
 from gpu_util import compare, run_gpu, run_oracle, to_gpu
 
@@ -30,6 +30,19 @@ def test_config_full_size(gpu_lib, cfg, nsample):
     out, lse, md, ns = run_gpu(w)
     bs = _sample(w.batch, nsample, cfg)
     compare(w, out, lse, run_oracle(w, batches=bs), batches=bs, label=f"c{cfg} full size, batches {len(bs)}")
+
+
+@pytest.mark.parametrize("cfg,n,nsample", [(2, 8, 8), (3, 8, 6), (5, 8, 4)])
+def test_batch_share_of_one_gpu(gpu_lib, cfg, n, nsample):
+    """One GPU's share of a batch split over n GPUs (its first B/n sequences
+    and their blocks, on the default number of parts): few sequences over
+    every compute unit, so each is cut into many short splits."""
+    print(f"config {cfg} share 1/{n}: generating", flush=True)
+    w = batch_share(make_config(cfg), n)
+    out, lse, md, ns = run_gpu(w)
+    assert int(ns[-1]) > 4 * w.batch                    # the case this covers: many splits per sequence
+    bs = _sample(w.batch, nsample, cfg)
+    compare(w, out, lse, run_oracle(w, batches=bs), batches=bs, label=f"c{cfg} share 1/{n}, batches {len(bs)}")
 
 
 def test_config4_long_sequence_last(gpu_lib):

@@ -11,5 +11,6 @@ from .mla_inputs import (  # noqa: F401
     fp8_query,
     make_config,
     make_workload,
+    batch_share,
     repage,
 )

@@ -240,3 +240,27 @@ def repage(w: Workload, page_block_size: int, seed: int = 0, pad: str = "nan") -
             kv[blk, :seg.shape[0]] = seg
         o += n
     return dataclasses.replace(w, name=f"{w.name}_ps{P}", block_table=bt, kv=kv, page_block_size=P)
+
+
+def batch_share(w: Workload, n: int, index: int = 0) -> Workload:
+    """One GPU's share when the batch is split evenly over n GPUs (data-
+    parallel attention): sequences index*B/n .. (index+1)*B/n - 1, their q
+    rows, and only their cache blocks, renumbered in pool order (the shuffled
+    placement is kept).  Table entries past a sequence's blocks become 0."""
+    if n < 1 or w.batch % n or not 0 <= index < n:
+        raise ValueError(f"batch {w.batch} does not split into {n} equal shares")
+    Bs = w.batch // n
+    rows = slice(index * Bs, (index + 1) * Bs)
+    P = w.page_block_size
+    L = w.cache_seqlens[rows]
+    nblk = [(int(x) + P - 1) // P for x in L]
+    bt_old = w.block_table[rows]
+    used = np.unique(np.concatenate([bt_old[b, :nblk[b]] for b in range(Bs)] + [np.zeros(0, np.int32)]))
+    used = used if used.size else np.zeros(1, np.int32)
+    remap = np.zeros(w.num_blocks, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    bt = np.zeros((Bs, max(1, max(nblk) if nblk else 1)), dtype=np.int32)
+    for b in range(Bs):
+        bt[b, :nblk[b]] = remap[bt_old[b, :nblk[b]]]
+    return dataclasses.replace(w, name=f"{w.name}_share{index}of{n}", batch=Bs, cache_seqlens=L.copy(),
+                               block_table=bt, q_bits=w.q_bits[rows].copy(), kv=w.kv[used])
