@@ -119,3 +119,18 @@ def test_bench_line_carries_the_contract_fields(gpu_lib):
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and 0.0 < roof["frac"] < 1.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert rec["config"]["workload"].startswith("standard MLA decode")
+
+
+@pytest.mark.gpu
+def test_bench_line_for_one_gpus_batch_share(gpu_lib):
+    """--batch-share N: the line describes the share (B/N sequences) and
+    carries no counter traffic (the committed counters are for the whole
+    batch)."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--batch-share", "8", "--steps", "3",
+                        "--warmup", "3", "--fwd-iters", "3", "--no-cpu-baseline"], capture_output=True, text=True,
+                       cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    assert rec["config"]["batch"] == 8 and rec["config"]["batch_share_of_gpus"] == 8
+    assert "share of the batch over 8 GPUs" in rec["config"]["workload"]
+    assert rec["roofline"]["traffic"] is None and rec["n_gpus"] == 1
