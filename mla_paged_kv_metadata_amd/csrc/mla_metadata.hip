@@ -30,52 +30,80 @@ constexpr int kT = kMetaThreads;
 
 __device__ __forceinline__ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// One step of a wave-wide inclusive scan of a 64-bit value held as two
+// dwords: add the value that the DPP control `ctrl` moves in (lanes without
+// a source, or in rows outside row_mask, add 0).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void scan_step(unsigned &lo, unsigned &hi) {
+  const unsigned ylo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)lo, kCtrl, kRowMask, 0xf, false);
+  const unsigned yhi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)hi, kCtrl, kRowMask, 0xf, false);
+  const unsigned nlo = lo + ylo;
+  hi = hi + yhi + (nlo < lo ? 1u : 0u);
+  lo = nlo;
+}
+// Inclusive scan over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 lanes
+// within each row of 16 (row_shr), then the last lane of row 0 / row 2 added
+// to rows 1 / 3 (row_bcast:15) and lane 31 added to rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ long long wave_inclusive_scan(long long v) {
+  unsigned lo = (unsigned)(unsigned long long)v, hi = (unsigned)((unsigned long long)v >> 32);
+  scan_step<0x111, 0xf>(lo, hi);
+  scan_step<0x112, 0xf>(lo, hi);
+  scan_step<0x114, 0xf>(lo, hi);
+  scan_step<0x118, 0xf>(lo, hi);
+  scan_step<0x142, 0xa>(lo, hi);
+  scan_step<0x143, 0xc>(lo, hi);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Exclusive scan over `n` int64 values held in smem[0..n), in place; smem[n] = total.
 // Each thread scans a contiguous chunk; chunk sums are scanned within each
-// wave by shuffles, then across the kT / 64 wave totals (held in `tmp`).
+// wave (wave_inclusive_scan), and every thread adds the totals of the waves
+// before its own (held in `tmp`).
 __device__ void block_exclusive_scan(long long *smem, int n, long long *tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + kT - 1) / kT;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   long long s = 0;
   for (int i = lo; i < hi; ++i) s += smem[i];
-  long long incl = s;                              // inclusive scan of chunk sums within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const long long incl = wave_inclusive_scan(s);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    long long run = 0;
-    for (int w = 0; w < kT / 64; ++w) {
-      const long long t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[kT / 64] = run;
+  long long before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kT / 64; ++w) {
+    const long long t = tmp[w];
+    before += w < wave ? t : 0;
+    total += t;
   }
-  __syncthreads();
-  long long run = tmp[wave] + incl - s;
+  long long run = before + incl - s;
   for (int i = lo; i < hi; ++i) {
     const long long x = smem[i];
     smem[i] = run;
     run += x;
   }
-  __syncthreads();
-  if (tid == 0) smem[n] = tmp[kT / 64];
-  __syncthreads();
+  if (tid == 0) smem[n] = total;
+  __syncthreads();                                 // (also: tmp is free again)
 }
 
-// largest b in [0, n] with pref[b] <= x  (pref strictly increasing because every cost >= 1)
-__device__ __forceinline__ int upper_index(const long long *pref, int n, long long x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= x) lo = mid; else hi = mid - 1;
+// Largest b in [0, n] with pref[b] <= x, for two keys at once (the two
+// searches' LDS reads overlap); pref is strictly increasing because every
+// cost is >= 1.
+__device__ __forceinline__ void upper_index2(const long long *pref, int n, long long x1, long long x2, int &r1,
+                                             int &r2) {
+  int lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
+  while (lo1 < hi1 || lo2 < hi2) {
+    const int m1 = (lo1 + hi1 + 1) >> 1, m2 = (lo2 + hi2 + 1) >> 1;
+    const long long v1 = pref[min(m1, n)], v2 = pref[min(m2, n)];
+    if (lo1 < hi1) {
+      if (v1 <= x1) lo1 = m1; else hi1 = m1 - 1;
+    }
+    if (lo2 < hi2) {
+      if (v2 <= x2) lo2 = m2; else hi2 = m2 - 1;
+    }
   }
-  return lo;
+  r1 = lo1;
+  r2 = lo2;
 }
 
 template <typename T>
@@ -110,12 +138,10 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
     };
     int b0 = -1, b1 = -1;
     if (u0 < u1) {
-      const int b = upper_index(pref, B, u0);
+      int b, e;
+      upper_index2(pref, B, u0, u1 - 1, b, e);
       b0 = works(b) ? b : (b + 1 < B && works(b + 1) ? b + 1 : -1);
-      if (b0 >= 0) {
-        const int e = upper_index(pref, B, u1 - 1);
-        b1 = works(e) ? e : e - 1;
-      }
+      if (b0 >= 0) b1 = works(e) ? e : e - 1;
     }
     row[5] = (int32_t)W;
     row[6] = fixed_cost;
