@@ -86,25 +86,39 @@ __device__ void block_exclusive_scan(long long *smem, int n, long long *tmp) {
   __syncthreads();                                 // (also: tmp is free again)
 }
 
-// Largest b in [0, n] with pref[b] <= x, for two keys at once (the two
-// searches' LDS reads overlap); pref is strictly increasing because every
-// cost is >= 1.
+// Largest b in [0, n] with pref[b] <= x, for two keys at once: binary
+// lifting from b = 0 (pref[0] = 0 <= x) with steps 2^k .. 1, 2^(k+1) > n, the
+// same number of steps in every lane and the two searches' LDS reads side by
+// side.  pref is strictly increasing because every cost is >= 1.
 __device__ __forceinline__ void upper_index2(const long long *pref, int n, long long x1, long long x2, int &r1,
                                              int &r2) {
-  int lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
-  while (lo1 < hi1 || lo2 < hi2) {
-    const int m1 = (lo1 + hi1 + 1) >> 1, m2 = (lo2 + hi2 + 1) >> 1;
-    const long long v1 = pref[min(m1, n)], v2 = pref[min(m2, n)];
-    if (lo1 < hi1) {
-      if (v1 <= x1) lo1 = m1; else hi1 = m1 - 1;
-    }
-    if (lo2 < hi2) {
-      if (v2 <= x2) lo2 = m2; else hi2 = m2 - 1;
-    }
+  int p1 = 0, p2 = 0;
+  for (int step = 1 << (31 - __builtin_clz((unsigned)n)); step > 0; step >>= 1) {
+    const long long v1 = pref[min(p1 + step, n)], v2 = pref[min(p2 + step, n)];
+    if (p1 + step <= n && v1 <= x1) p1 += step;
+    if (p2 + step <= n && v2 <= x2) p2 += step;
   }
-  r1 = lo1;
-  r2 = lo2;
+  r1 = p1;
+  r2 = p2;
 }
+
+// Division of values in [0, 2^32) by a divisor d >= 1 that every lane shares:
+// with m = floor((2^32 - 1) / d), mulhi(n, m) is floor(n / d) or at most 2
+// below it, and two corrections finish it.
+struct FastDiv {
+  unsigned d, m;
+  __device__ explicit FastDiv(unsigned dd) : d(dd), m(0xffffffffu / dd) {}
+  __device__ __forceinline__ unsigned operator()(unsigned n) const {
+    unsigned q = __umulhi(n, m);
+    unsigned r = n - q * d;
+    if (r >= d) {
+      ++q;
+      r -= d;
+    }
+    if (r >= d) ++q;
+    return q;
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
@@ -116,8 +130,17 @@ __device__ __forceinline__ void fill_rows(int B, int num_parts, int fixed_cost,
   const T total = (T)pref[B];
   const T P = num_parts;
   const T W = max((T)1, (total + P - 1) / P);                 // most units of one part
-  auto bound = [&](T p) -> T { return p * total / P; };
-  auto part_of = [&](T u) -> T { return ((u + 1) * P - 1) / total; };   // u < total
+  // 32-bit instance: every product below stays under 2^31 (checked by the
+  // caller), so the divisions by P and by total use FastDiv.
+  [[maybe_unused]] const FastDiv div_p(sizeof(T) == 4 ? (unsigned)P : 1u), div_t(sizeof(T) == 4 ? (unsigned)total : 1u);
+  auto bound = [&](T p) -> T {
+    if constexpr (sizeof(T) == 4) return (T)div_p((unsigned)(p * total));
+    else return p * total / P;
+  };
+  auto part_of = [&](T u) -> T {                             // u < total
+    if constexpr (sizeof(T) == 4) return (T)div_t((unsigned)((u + 1) * P - 1));
+    else return ((u + 1) * P - 1) / total;
+  };
 
   for (int b = tid; b < B; b += kT) {
     const T nblk = (T)(pref[b + 1] - pref[b]) - fc;
