@@ -259,16 +259,6 @@ __device__ __forceinline__ void zero_tail_rows_fp8(LDS_AS uint8_t *page, int nva
   }
 }
 
-// Eight e4m3fn codes -> eight bf16 (exact: every e4m3fn value is a bf16
-// value), two per instruction.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
-  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
-                                          __builtin_bit_cast(unsigned, c), __builtin_bit_cast(unsigned, d)});
-}
 template <bool kSplit, int k>
 __device__ __forceinline__ void dma_fp8_step(const PageSrc &p, LDS_AS uint8_t *dst, int wave) {
   if constexpr (kSplit && k == 8) lds_dma16<0>(p.rope_even, dst + (4 * k + wave) * 1024);
@@ -340,19 +330,13 @@ __device__ __forceinline__ void mfma_zero_all(f32x16 (&o)[kOTiles]) {
 // takes an inline zero accumulator; the destination is early-clobber (a
 // 32x32 MFMA destination may not overlap its A/B sources).  mfma_qk_drain
 // supplies the wait states between the last matrix-core write of S^T and
-// its first VALU read (19 > the 8-pass XDL requirement).
-// kFresh: the A operand was just written by VALU (a converted fp8
-// fragment); the compiler does not see into the asm, so the 2 wait states a
-// VALU-written VGPR needs before an MFMA reads it are supplied here.
-template <bool kFresh = false>
+// its first VALU read (19 > the 8-pass XDL requirement).  The A operands
+// come straight from LDS reads, never from a VALU write just before.
 __device__ __forceinline__ void mfma_qk_first(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
-  if constexpr (kFresh) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
 }
-template <bool kFresh = false>
 __device__ __forceinline__ void mfma_qk(f32x16 &s, const bf16x8 &a, const bf16x8 &b) {
-  if constexpr (kFresh) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-  else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_qk_drain(f32x16 &s) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s));
@@ -390,7 +374,7 @@ __device__ __forceinline__ void scale_scores(f32x16 &sc, float d) {
 // Returns true (wave-uniform) when some row of this wave needs a re-run.
 //   scale_log2 > 0 (softmax_scale * log2 e, clamped away from 0 by the caller);
 //   mask: some key of this page may be invisible to some row of the wave.
-template <bool kFp8, bool kSplit>
+template <bool kSplit>
 __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16x8 (&qf)[kKSteps],
                                             f32x16 (&o)[kOTiles], float &m, float &l, float &m_restart,
                                             int lane, int key0, int nvis, float scale_log2, bool mask,
@@ -422,47 +406,17 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   const LDS_AS uint8_t *va_even = pg + la + 64 * t1, *va_odd = pg + la + 64 * (1 - t1);
   const LDS_AS uint8_t *vb_even = pg + lb + 64 * t1, *vb_odd = pg + lb + 64 * (1 - t1);
 
-  // fp8 page (the layout of page_src_fp8): K of token r, codes 16 ks + 8 hl
-  // .. +7 at 4096 (ks / 4) + 64 r + 16 ((ks % 4) ^ ((r / 4) % 4)) + 8 hl
-  // (+2048 for tile 1): four lane bases.  V^T by 8-bit transposing reads: in
-  // each 16-lane group G, output lane i gets byte i % 8 of the 8-byte rows
-  // loaded by lanes 2 e + i / 8 (e = 0..7, its k-slots); for the k-slot order
-  // of P^T (slot e of lane half h is token 8 (e / 4) + 4 h + e % 4 of the
-  // k-step) source lane (G, s) loads token 16 ks + 8 (s / 8) + 4 (G / 2) +
-  // (s / 2) % 4, codes 32 mt + 16 (G % 2) + 8 (s % 2) .. +7: two lane bases
-  // (even / odd mt) plus immediates.
-  const int f_sw = (r >> 2) & 3;
-  const LDS_AS uint8_t *kb8[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) kb8[v] = pg + 64 * r + 16 * (v ^ f_sw) + 8 * hl;
-  const int fa = s16 >> 3, fb = g >> 1, fc = (s16 >> 1) & 3;
-  const int f_lane = 64 * (8 * fa + 4 * fb + fc) + 8 * (s16 & 1);
-  const LDS_AS uint8_t *v8[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) v8[par] = pg + f_lane + 16 * ((2 * par + (g & 1)) ^ (2 * fa + fb));
-
   // LDS operand loads run ahead of their MFMAs (software pipeline); loads
-  // complete in order, so each MFMA waits only for its own operand.  An fp8
-  // operand stays as 8 codes (two VGPRs) until just before its MFMA.
+  // complete in order, so each MFMA waits only for its own operand.
   auto kload = [&](int ks, int tile) {
-    if constexpr (kFp8) return *(const LDS_AS u32x2 *)(kb8[ks & 3] + 4096 * (ks >> 2) + 2048 * tile);
-    else return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + tile * 4096);
+    return *(const LDS_AS bf16x8 *)(kb[ks & 3] + 8192 * (ks >> 2) + tile * 4096);
   };
   auto vload = [&](int step) {
     const int ks = step >> 4, mt = step & 15;         // k-step of 16 tokens, 32-dim output tile
-    if constexpr (kFp8) {
-      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (LDS_AS v2i32 *)(v8[mt & 1] + 4096 * (mt >> 1) + 1024 * ks)));
-    } else {
-      const int ofs = 8192 * (mt >> 1) + 2048 * ks;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-  auto cook = [&](auto raw) -> bf16x8 {
-    if constexpr (kFp8) return fp8x8_to_bf16(raw);
-    else return raw;
+    const int ofs = 8192 * (mt >> 1) + 2048 * ks;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? va_odd : va_even) + ofs));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(((mt & 1) ? vb_odd : vb_even) + ofs));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   // Online softmax of one 32-token tile, in kSoftPieces pieces that are
@@ -525,7 +479,7 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // prefetched kPre steps ahead; the tile-0 softmax runs under the tile-1
   // chain.
   constexpr int kPre = 4;
-  constexpr int kDmaEvery = 2 * kKSteps / (kFp8 ? kF8PageLoads : kPageLoads);   // 4 (bf16) or 8 (fp8)
+  constexpr int kDmaEvery = 2 * kKSteps / kPageLoads;   // 4
   decltype(kload(0, 0)) kf[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) kf[i] = kload(i, 0);
@@ -537,13 +491,10 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // instruction of the next page.
   auto qk_step = [&](f32x16 &sc, int tile, int ks) {
     const int g = tile * kKSteps + ks, sl = g % kPre;
-    if (ks == 0) mfma_qk_first<kFp8>(sc, cook(kf[sl]), qf[0]);
-    else mfma_qk<kFp8>(sc, cook(kf[sl]), qf[ks]);
+    if (ks == 0) mfma_qk_first(sc, kf[sl], qf[0]);
+    else mfma_qk(sc, kf[sl], qf[ks]);
     if (g + kPre < 2 * kKSteps) kf[sl] = kload((g + kPre) % kKSteps, (g + kPre) / kKSteps);
-    if (nx.valid && g % kDmaEvery == 0) {
-      if (kFp8) dma_fp8_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
-      else dma_bf16_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
-    }
+    if (nx.valid && g % kDmaEvery == 0) dma_bf16_dispatch<kSplit>(nx.src, nx.dst, nx.wave, g / kDmaEvery);
   };
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
@@ -564,8 +515,8 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   }
   // First V^T operands.
   // V^T operands run 3 MFMAs ahead: same-box A/B against 4 ahead, MTP causal
-  // decode 341 -> 335 us, standard decode 62.9 -> 62.3 us, fp8 287 -> 286 us;
-  // 6 ahead spills registers and was slower.
+  // decode 341 -> 335 us, standard decode 62.9 -> 62.3 us; 6 ahead spills
+  // registers and was slower.
   constexpr int kVPre = 3;
   decltype(vload(0)) vraw[kVPre];
 #pragma unroll
@@ -575,7 +526,7 @@ __device__ __forceinline__ bool attend_page(const LDS_AS uint8_t *pg, const bf16
   // under the first two k-steps (tile 0's P), which do not need it.
   auto pv_step = [&](int step) {
     const int sl = step % kVPre;
-    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cook(vraw[sl]), pb[step >> 4], o[step & 15], 0, 0, 0);
+    o[step & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vraw[sl], pb[step >> 4], o[step & 15], 0, 0, 0);
     if (step + kVPre < 4 * kOTiles) vraw[sl] = vload(step + kVPre);
   };
   constexpr int kSoftCN = 2 * kOTiles - 2;
@@ -802,7 +753,6 @@ __device__ __forceinline__ void quantize_q_f8(i32x8 (&q8)[18], int &s_hi, int &s
 // where the value is used.
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(int &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(unsigned &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin_elem(f32x16 &v, int i) {
   float x = v[i];
   pin(x);
@@ -1535,7 +1485,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeArg
               need |= attend_tile<kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage + 32 * wave, nvis, scale_log2,
                                   (j + 1) * kPage > nvis_min, desc_tab, descale, nx, wave);
             else
-              need |= attend_page<false, kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
+              need |= attend_page<kSplit>(pg, qf, o, m, l, m_restart, lane, j * kPage, nvis, scale_log2,
                                                  (j + 1) * kPage > nvis_min, desc_tab, descale, nx);
           } else if (nx.valid) {                    // a wave without rows still copies its share
             if (kFp8) dma_page_fp8<kSplit>(nx.src, nx.dst, wave);
