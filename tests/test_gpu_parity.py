@@ -86,3 +86,20 @@ def test_scheduler_kernel_on_huge_lengths(gpu_lib, parts):
     ref_md, ref_ns = schedule(L, parts, 4)
     assert np.array_equal(ns.cpu().numpy(), ref_ns)
     assert np.array_equal(md.cpu().numpy(), ref_md)
+
+
+@pytest.mark.parametrize("B,parts,fc", [(65, 256, 4), (129, 256, 2), (300, 97, 4), (5000, 256, 3), (8192, 1024, 4)])
+def test_scheduler_kernel_on_large_batches(gpu_lib, B, parts, fc):
+    """Batches past one wave (65, 129), past one value per thread (300 over
+    256 threads) and up to the batch limit: the block scans cross waves and
+    chunks; the table must still be the schedule rule's, bit for bit."""
+    rng = np.random.default_rng(B)
+    L = rng.integers(0, 9000, size=B).astype(np.int32)
+    L[rng.integers(0, B, size=max(1, B // 10))] = 0
+    sl = torch.from_numpy(L).cuda()
+    import mla_paged_kv_metadata_amd as mla
+    md, ns = mla.mla_get_metadata(sl, 128, 1, num_parts=parts, fixed_cost=fc)
+    torch.cuda.synchronize()
+    ref_md, ref_ns = schedule(L, parts, fc)
+    assert np.array_equal(ns.cpu().numpy(), ref_ns)
+    assert np.array_equal(md.cpu().numpy(), ref_md)
