@@ -141,3 +141,16 @@ def test_two_waves_per_page_for_few_rows(gpu_lib, H, s_q, causal, parts):
                       causal=causal, seed=107 + H)
     out, lse, _, _ = run_gpu(w, num_parts=parts)
     compare(w, out, lse, run_oracle(w), label=f"few rows H={H} s_q={s_q} parts={parts}")
+
+
+@pytest.mark.parametrize("kv_dtype,num_heads_k,parts", [("bf16", 1, None), ("fp8_e4m3fn", 1, None), ("bf16", 2, 16)])
+def test_the_most_rows_per_kv_head(gpu_lib, kv_dtype, num_heads_k, parts):
+    """s_q x heads per KV head at the boundary's limit (1024 rows: eight
+    128-row tiles per KV head, MTP with 8 query tokens, causal), on the
+    default and on few parts."""
+    H = 128 * num_heads_k
+    w = make_workload(seqlens=[700, 9, 1500], s_q=8, num_heads_q=H, num_heads_k=num_heads_k, causal=True,
+                      kv_dtype=kv_dtype, seed=81 + num_heads_k)
+    assert w.heads_per_head_k == 1024
+    out, lse, _, _ = run_gpu(w, num_parts=parts)
+    compare(w, out, lse, run_oracle(w), label=f"1024 rows {kv_dtype} H_k={num_heads_k}")
