@@ -420,7 +420,10 @@ def main():
     dev = torch.device("cuda:0")
     w = make_config(args.config)
     if args.batch_share > 1:
-        w = batch_share(w, args.batch_share)
+        try:
+            w = batch_share(w, args.batch_share)
+        except ValueError as e:
+            raise SystemExit(f"--batch-share {args.batch_share}: {e}")
     if args.page_block_size != w.page_block_size:
         w = repage(w, args.page_block_size, seed=1)
     fp8 = w.kv_dtype == "fp8_e4m3fn"
